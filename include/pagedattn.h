@@ -1,0 +1,254 @@
+/*
+ * libpagedattn -- paged-KV varlen flash attention for AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels.  Every pointer argument documented
+ * as "device" is a HIP device pointer; "host" pointers are ordinary host
+ * memory.  The library allocates no memory, keeps no global state and never
+ * synchronises: each device-side call enqueues its kernels on the caller's
+ * `stream` and returns at once, so the calls can be captured into a HIP
+ * graph.  All argument checks run on the host BEFORE any HIP call; a call
+ * that returns an error has launched nothing.
+ *
+ * Data types: Q/K/V/out are bf16 (stored as 16-bit words), lse is fp32.
+ * The KV cache is one contiguous tensor laid out (2, num_blocks, block_size,
+ * num_kv_heads, head_size): plane 0 holds keys, plane 1 values (the
+ * FlashAttention backend class hierarchy in "FlashAttention 在 vLLM 中的实现分析",
+ * section 2.1, and the `kv_cache.unbind(dim=0)` split of section 4).
+ *
+ * Semantics fixed where the pages are silent:
+ *   - GQA: query head h reads KV head h / (num_heads / num_kv_heads).
+ *   - causal masking is bottom-right aligned: query i (0-based) of a sequence
+ *     with Lq queries and Lk keys sees keys j <= i + Lk - Lq.
+ *   - lse is the natural-log log-sum-exp of the scaled scores (the backend
+ *     abstraction page warns that ln and log2 LSE must not be mixed).
+ *   - a query that sees no key gets out = 0 and lse = -inf.
+ */
+#ifndef PAGEDATTN_H_
+#define PAGEDATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, inconsistent lengths */
+  PA_ERR_UNSUPPORTED = 2,        /* a valid configuration this build does not instantiate */
+  PA_ERR_WORKSPACE_TOO_SMALL = 3,/* worklist or workspace smaller than the plan needs */
+  PA_ERR_HIP = 4                 /* a kernel launch failed (hipGetLastError) */
+} pa_status;
+
+/* Static string naming a status code. */
+const char* pa_status_str(pa_status s);
+
+/* Library version, (major << 16) | minor. */
+int32_t pa_version(void);
+
+/* Head sizes with a compiled kernel. */
+#define PA_NUM_HEAD_SIZES 3
+extern const int32_t pa_supported_head_sizes[PA_NUM_HEAD_SIZES]; /* {64, 128, 256} */
+
+/* Shape of one attention call.
+ *   batch              number of sequences B
+ *   num_heads          query heads H
+ *   num_kv_heads       KV heads Hkv; H % Hkv == 0
+ *   head_size          D, one of pa_supported_head_sizes
+ *   block_size         BS, tokens per cache block; a positive multiple of 16
+ *                      (the FlashAttention backend rejects other sizes:
+ *                      "FlashAttention と FlashInfer" page, 境界と失敗)
+ *   num_blocks         NB, physical blocks in the cache
+ *   max_blocks_per_seq columns of block_table a sequence may use
+ *   block_table_stride int32 elements between block_table rows; 0 means
+ *                      max_blocks_per_seq (a column slice such as the cascade
+ *                      suffix view block_table[:, k:] keeps the full stride)
+ *   causal             0 or 1
+ *   scale              softmax scale applied to q.k (fp32)            */
+typedef struct {
+  int32_t batch;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t head_size;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t block_table_stride;
+  int32_t causal;
+  float scale;
+} pa_attn_params;
+
+/* ------------------------------------------------------------------------
+ * pa_plan_varlen -- host-side scheduling metadata (the ahead-of-time
+ * schedule of "FlashAttention 在 vLLM 中的实现分析", section 7: computed from
+ * batch size, query/key lengths, head counts, head size and page size, so
+ * the kernels run a fixed, deterministic work list).
+ *
+ * Host only; makes no HIP call.  Reads host mirrors of cu_seqlens_q [B+1]
+ * (cu[0] == 0, non-decreasing) and seqused_k [B] (0 <= Lk <=
+ * max_blocks_per_seq * block_size).
+ *   force_splits     0: the planner chooses how many KV splits each work unit
+ *                    gets (for PA_PLAN_TARGET_CUS compute units);
+ *                    n >= 1: every unit is split into n ranges (ranges
+ *                    shorter than one key tile are merged) -- for tests of
+ *                    the split-KV reduction
+ *   host_worklist    receives the int32 work list (layout below); may be
+ *                    NULL to query sizes only
+ *   worklist_capacity_bytes  size of host_worklist
+ *   info             receives item counts and the worklist / workspace sizes
+ * The caller copies the work list unchanged to device memory and passes it,
+ * with `info`, to pa_varlen_fwd.
+ * Errors: PA_ERR_INVALID_ARGUMENT (bad params or lengths),
+ * PA_ERR_UNSUPPORTED (head size), PA_ERR_WORKSPACE_TOO_SMALL (capacity).
+ * ------------------------------------------------------------------------ */
+#define PA_PLAN_TARGET_CUS 256
+
+typedef struct {
+  int32_t num_small_items;   /* items for the small-row (decode) kernel     */
+  int32_t num_tiled_items;   /* items for the 128-row tiled kernel           */
+  int32_t num_reduce_items;  /* split-KV merges                              */
+  int32_t num_partial_rows;  /* fp32 partial rows held in the workspace      */
+  int32_t batch, num_heads, num_kv_heads, head_size, causal, num_tokens;
+  size_t worklist_bytes;
+  size_t workspace_bytes;
+} pa_plan_info;
+
+pa_status pa_plan_varlen(const pa_attn_params* p,
+                         const int32_t* host_cu_seqlens_q,
+                         const int32_t* host_seqused_k,
+                         int32_t force_splits,
+                         int32_t* host_worklist, size_t worklist_capacity_bytes,
+                         pa_plan_info* info);
+
+/* ------------------------------------------------------------------------
+ * pa_cascade_split -- host-side metadata of the two cascade passes
+ * ("FlashAttention 在 vLLM 中的实现分析", section 6.3): a prefix pass in
+ * which all num_tokens queries form ONE pseudo-sequence attending
+ * non-causally to the common_prefix_len shared keys addressed by block-table
+ * row 0, and a suffix pass in which every sequence attends causally to its
+ * own remaining keys through block_table[:, common_prefix_len/BS:].
+ *
+ *   p                  the full (single-pass) problem; must be causal
+ *   common_prefix_len  > 0, a multiple of block_size, and <= Lk_b - Lq_b for
+ *                      every sequence (each query comes after the prefix)
+ *   host_cu_seqlens_q, host_seqused_k   host mirrors [B+1], [B]
+ * Outputs (host):
+ *   prefix_p, suffix_p     params of the two passes
+ *   prefix_cu_seqlens_q    [2] = {0, num_tokens}
+ *   prefix_seqused_k       [1] = {common_prefix_len}
+ *   suffix_seqused_k       [B] = seqused_k - common_prefix_len
+ *   block_table_col0       column offset of the suffix view
+ * The caller uploads the three small arrays, plans and runs each pass with
+ * pa_varlen_fwd (prefix with block_table, suffix with block_table +
+ * *block_table_col0) and merges with pa_merge_attn_states.  Host only.
+ * ------------------------------------------------------------------------ */
+pa_status pa_cascade_split(const pa_attn_params* p, int32_t common_prefix_len,
+                           const int32_t* host_cu_seqlens_q, const int32_t* host_seqused_k,
+                           pa_attn_params* prefix_p, pa_attn_params* suffix_p,
+                           int32_t* prefix_cu_seqlens_q, int32_t* prefix_seqused_k,
+                           int32_t* suffix_seqused_k, int32_t* block_table_col0);
+
+/* ------------------------------------------------------------------------
+ * pa_reshape_and_cache -- scatter the new tokens' keys and values into the
+ * paged cache ("FlashAttention 在 vLLM 中的实现分析", section 4.2, the
+ * do_kv_cache_update step, and the helper-kernel table of section 8.2).
+ *
+ *   key, value        device bf16 [num_tokens, num_kv_heads, head_size];
+ *                     head_size contiguous, heads contiguous; consecutive
+ *                     tokens key_row_stride / value_row_stride elements
+ *                     apart (>= num_kv_heads * head_size, multiple of 8)
+ *   kv_cache          device bf16 (2, num_blocks, block_size, Hkv, D), updated
+ *                     in place
+ *   slot_mapping      device int64 [num_tokens]; token t goes to block
+ *                     slot / block_size, offset slot % block_size; a negative
+ *                     slot skips the token.  Slots must be < num_blocks *
+ *                     block_size and distinct (not checked on the device).
+ * Bit copy: the written bits equal the input bits.
+ * num_tokens == 0 launches nothing and returns PA_OK.
+ * ------------------------------------------------------------------------ */
+pa_status pa_reshape_and_cache(const void* key, const void* value,
+                               int64_t key_row_stride, int64_t value_row_stride,
+                               void* kv_cache, const int64_t* slot_mapping,
+                               int32_t num_tokens, int32_t num_kv_heads, int32_t head_size,
+                               int32_t num_blocks, int32_t block_size, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * pa_varlen_fwd -- paged varlen flash attention forward
+ * ("FlashAttention 在 vLLM 中的实现分析", section 4 standard call and section 5:
+ * q packed [num_tokens, H, D] and delimited by cu_seqlens_q, keys of
+ * sequence b are its first seqused_k[b] cache positions, addressed through
+ * block_table[b][j / block_size]; tiling with an online softmax, section
+ * 1.1; split-KV partials merged by LSE, section 1.3 num_splits).
+ *
+ *   p                 shape, as given to pa_plan_varlen
+ *   plan              the info pa_plan_varlen filled for these lengths
+ *   worklist          device copy of the planned work list (plan->worklist_bytes)
+ *   q                 device bf16 [num_tokens, H, D], contiguous
+ *   kv_cache          device bf16 (2, NB, BS, Hkv, D), contiguous
+ *   cu_seqlens_q      device int32 [B+1]
+ *   seqused_k         device int32 [B]
+ *   block_table       device int32 [B, max_blocks_per_seq]; entries at
+ *                     index < ceil(seqused_k[b] / BS) must be in [0, NB);
+ *                     the rest are never read
+ *   num_tokens        cu_seqlens_q[B]
+ *   out               device bf16 [num_tokens, H, D]; every element is written
+ *   lse               device fp32 [num_tokens, H] (natural log), or NULL
+ *   workspace         device scratch, >= plan->workspace_bytes, 256-byte
+ *                     aligned (may be NULL when that is 0)
+ * The device lengths must equal the host mirrors given to the planner.
+ * Errors: PA_ERR_INVALID_ARGUMENT (null pointer, plan/params mismatch),
+ * PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE_TOO_SMALL, PA_ERR_HIP.
+ * ------------------------------------------------------------------------ */
+pa_status pa_varlen_fwd(const pa_attn_params* p, const pa_plan_info* plan,
+                        const int32_t* worklist,
+                        const void* q, const void* kv_cache,
+                        const int32_t* cu_seqlens_q, const int32_t* seqused_k,
+                        const int32_t* block_table,
+                        int32_t num_tokens, void* out, float* lse,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * pa_merge_attn_states -- LSE-weighted merge of two partial attentions over
+ * disjoint key sets (the cascade's third step, "FlashAttention 在 vLLM 中的
+ * 实现分析" section 6.3, and the merge_attn_states helper of section 8.2):
+ *   M = max(lse_p, lse_s), a = exp(lse_p - M), b = exp(lse_s - M),
+ *   out = (a * out_p + b * out_s) / (a + b), out_lse = M + ln(a + b);
+ *   two empty partials (both -inf) give out = 0, out_lse = -inf.
+ *
+ *   out, prefix_out, suffix_out   device bf16 [num_tokens, num_heads, head_size]
+ *                                 (out may alias either input)
+ *   out_lse                       device fp32 [num_tokens, num_heads] or NULL
+ *   prefix_lse, suffix_lse        device fp32 [num_tokens, num_heads]
+ * head_size must be a multiple of 8 and at most 512.
+ * ------------------------------------------------------------------------ */
+pa_status pa_merge_attn_states(void* out, float* out_lse,
+                               const void* prefix_out, const float* prefix_lse,
+                               const void* suffix_out, const float* suffix_lse,
+                               int32_t num_tokens, int32_t num_heads, int32_t head_size,
+                               hipStream_t stream);
+
+/* Work-list layout (int32 words):
+ *   [0] PA_WORKLIST_MAGIC  [1] version  [2] num_small_items  [3] num_tiled_items
+ *   [4] num_reduce_items  [5] num_partial_rows  [6] group size H/Hkv
+ *   [7] causal  [8..15] reserved (0)
+ * then num_small_items + num_tiled_items attention items, then the reduce
+ * items, PA_ITEM_WORDS words each.
+ * attention item: seq, kv_head, row0, nrows, kv_begin, kv_end,
+ *   partial_row (-1: write out/lse directly), 0
+ * reduce item: seq, kv_head, row0, nrows, partial_row0, num_splits, 0, 0
+ *   (split s of the unit wrote rows partial_row0 + s * nrows ...)
+ * A "row" of sequence b is (query token i, head-in-group g) -> row i*G + g,
+ * G = H / Hkv; kv_head's query heads are kv_head*G .. kv_head*G + G-1.    */
+#define PA_WORKLIST_MAGIC 0x50414731
+#define PA_WORKLIST_VERSION 1
+#define PA_WORKLIST_HEADER_WORDS 16
+#define PA_ITEM_WORDS 8
+#define PA_SMALL_MAX_ROWS 16
+#define PA_TILED_ROWS 128
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGEDATTN_H_ */

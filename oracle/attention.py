@@ -85,15 +85,15 @@ def _visible(Lq: int, Lk: int, causal: bool) -> np.ndarray:
     return j <= i + (Lk - Lq)
 
 
-def gather_kv(kv_cache_f64: np.ndarray, block_table_row: np.ndarray, Lk: int):
+def gather_kv(kv_cache: np.ndarray, block_table_row: np.ndarray, Lk: int):
     """Keys/values 0..Lk-1 of one sequence: key j lives in physical block
     ``block_table_row[j // BS]`` at offset ``j % BS``.  Returns (K, V), each
-    [Lk, Hkv, D]."""
-    BS = kv_cache_f64.shape[2]
+    [Lk, Hkv, D], in the cache's dtype."""
+    BS = kv_cache.shape[2]
     j = np.arange(Lk)
     phys = block_table_row[j // BS]
     off = j % BS
-    return kv_cache_f64[0, phys, off], kv_cache_f64[1, phys, off]
+    return kv_cache[0, phys, off], kv_cache[1, phys, off]
 
 
 def _softmax_rows(s: np.ndarray, vis: np.ndarray, v: np.ndarray):
@@ -130,7 +130,6 @@ def varlen_attention(q: np.ndarray, kv_cache: np.ndarray, cu_seqlens_q: np.ndarr
     Hkv = kv_cache.shape[3] if num_kv_heads is None else num_kv_heads
     scale = float(np.float32(scale))
     qf = bf16_to_f64(q)
-    cf = bf16_to_f64(kv_cache)
     out = np.zeros((T, H, D), dtype=np.float64)
     lse = np.full((T, H), NEG_INF, dtype=np.float64)
     B = len(seqused_k)
@@ -139,7 +138,8 @@ def varlen_attention(q: np.ndarray, kv_cache: np.ndarray, cu_seqlens_q: np.ndarr
         Lq, Lk = t1 - t0, int(seqused_k[b])
         if Lq == 0:
             continue
-        K, V = gather_kv(cf, np.asarray(block_table[b]), Lk)
+        Kb, Vb = gather_kv(kv_cache, np.asarray(block_table[b]), Lk)
+        K, V = bf16_to_f64(Kb), bf16_to_f64(Vb)
         vis = _visible(Lq, Lk, causal)
         for h in range(H):
             kvh = _kv_head(h, H, Hkv)

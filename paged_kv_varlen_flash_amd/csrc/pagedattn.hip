@@ -1,0 +1,766 @@
+// libpagedattn -- HIP kernels for gfx950 (MI355X) and the C entry points.
+//
+// Kernels:
+//   reshape_and_cache_kernel   scatter new K/V rows into the paged cache by
+//                              slot_mapping ("FlashAttention 在 vLLM 中的实现分析",
+//                              sections 4.2 and 8.2)
+//   attn_small_kernel<D>       paged attention for work items of <= 16 rows
+//                              (decode: one token x the G query heads of a KV
+//                              head), bound by HBM reads of K/V
+//   attn_tiled_kernel<D>       paged attention for 128-row blocks (prefill),
+//                              bound by the matrix cores
+//   split_reduce_kernel<D>     LSE merge of split-KV partials (section 1.3
+//                              num_splits)
+//   merge_states_kernel        two-way LSE merge (section 6.3, step 3)
+//
+// Both attention kernels compute S^T = K Q^T and O^T = V^T P^T with bf16
+// MFMA and fp32 accumulation, so that every lane owns one query row: its
+// running max, its row sum and its slice of O^T never leave the lane except
+// for one cross-lane max/sum between the lanes that split the row's keys.
+// K is read from memory in its natural [key][d] layout as the A operand of
+// the first product; V is staged row-major in LDS and read back transposed
+// with ds_read_b64_tr_b16, which hands each lane four keys of one d column.
+// The softmax works in the log2 domain (scores pre-multiplied by
+// scale*log2(e), exp2), and converts the LSE to natural log on output.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "pagedattn.h"
+#include "plan_internal.h"
+
+namespace {
+
+typedef short bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// fp32 pair -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+__device__ __forceinline__ bf16x8_t pack_bf16x8(const float* p) {
+  uint4 w;
+  w.x = pack_bf16x2(p[0], p[1]);
+  w.y = pack_bf16x2(p[2], p[3]);
+  w.z = pack_bf16x2(p[4], p[5]);
+  w.w = pack_bf16x2(p[6], p[7]);
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
+__device__ __forceinline__ bf16x8_t ld16(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
+}
+
+__device__ __forceinline__ bf16x8_t zero8() {
+  bf16x8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
+  return z;
+}
+
+// transposing LDS read: within each 16-lane group, lane r receives element
+// r%4 of the 8-byte rows addressed by lanes r/4, r/4+4, r/4+8, r/4+12
+__device__ __forceinline__ bf16x4_t lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t*)(p));
+}
+
+__device__ __forceinline__ bf16x8_t cat(bf16x4_t a, bf16x4_t b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask));
+}
+
+struct Item {
+  int seq, kvh, row0, nrows, kv0, kv1, prow;
+};
+
+__device__ __forceinline__ Item load_item(const int32_t* p) {
+  Item it;
+  it.seq = p[0];
+  it.kvh = p[1];
+  it.row0 = p[2];
+  it.nrows = p[3];
+  it.kv0 = p[4];
+  it.kv1 = p[5];
+  it.prow = p[6];
+  return it;
+}
+
+struct AttnArgs {
+  const int32_t* items;
+  const uint16_t* q;
+  const uint16_t* cache;
+  const int32_t* cu;
+  const int32_t* seqused_k;
+  const int32_t* block_table;
+  uint16_t* out;
+  float* lse;
+  float* part_o;
+  float* part_lse;
+  int64_t plane;      // elements in one cache plane (NB*BS*Hkv*D)
+  int H, Hkv, G, BS, MB, bt_stride, causal;
+  float scale_log2;   // scale * log2(e)
+};
+
+// ---------------------------------------------------------------------------
+// reshape_and_cache: one thread per 16-byte chunk; consecutive threads take
+// consecutive chunks of one token's K (then V) row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const uint16_t* __restrict__ key, const uint16_t* __restrict__ value, int64_t key_stride,
+    int64_t value_stride, uint16_t* __restrict__ cache, const int64_t* __restrict__ slot_mapping,
+    int64_t total_chunks, int32_t chunks_per_row, int64_t row_elems, int64_t plane) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= total_chunks) return;
+  const int64_t tw = gid / chunks_per_row;      // token * 2 + which
+  const int32_t c = (int32_t)(gid - tw * chunks_per_row);
+  const int64_t t = tw >> 1;
+  const int which = (int)(tw & 1);
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0) return;
+  const uint16_t* src = which ? value + t * value_stride : key + t * key_stride;
+  uint16_t* dst = cache + (which ? plane : 0) + slot * row_elems;
+  reinterpret_cast<uint4*>(dst)[c] = reinterpret_cast<const uint4*>(src)[c];
+}
+
+// ---------------------------------------------------------------------------
+// Small-row attention: one workgroup of 4 waves per work item of <= 16 rows.
+// Each wave takes 32-key steps (wave w: keys kv0 + 32*(w + 4i) ...), so a
+// step is 2 MFMA tiles of 16 keys.  Lane (n = lane%16, g = lane/16) owns
+// query row n; for the QK^T product it loads K row (step + n) and
+// (step + 16 + n), d range [g*D/4, (g+1)*D/4), straight from the cache into
+// registers (the MFMA A operand), and the V rows of the same keys, which it
+// stages in its wave's LDS tile for the transposing read.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
+  constexpr int NT = D / 32;        // 16-byte pieces per lane per key row = QK k-steps
+  constexpr int NDT = D / 16;       // 16-wide d tiles of O^T
+  constexpr int VP = D + 16;        // LDS pitch of a V row (elements)
+  constexpr int DQ = D / 4;         // d range per lane group
+  constexpr int V_ELEMS = 4 * 32 * VP;
+  constexpr int EPI_FLOATS = 4 * 16 * D + 2 * 64;
+  constexpr int SMEM_BYTES = (V_ELEMS * 2 > EPI_FLOATS * 4) ? V_ELEMS * 2 : EPI_FLOATS * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[SMEM_BYTES];
+  uint16_t* smem = reinterpret_cast<uint16_t*>(smem_raw);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const Item it = load_item(a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS);
+  const int t0 = a.cu[it.seq];
+  const int Lq = a.cu[it.seq + 1] - t0;
+  const int Lk = a.seqused_k[it.seq];
+  const int G = a.G;
+  const int nrows = min(it.nrows, Lq * G - it.row0);
+  const int kv1 = min(min(it.kv1, Lk), a.MB * a.BS);
+  const int kv0 = it.kv0;
+
+  const int r = it.row0 + n;
+  const bool row_ok = n < nrows;
+  const int tok = r / G;
+  const int head = it.kvh * G + (r - tok * G);
+  const int row_limit = a.causal ? tok + Lk - Lq : INT_MAX;
+
+  bf16x8_t qf[NT];
+  if (row_ok) {
+    const uint16_t* qp = a.q + ((int64_t)(t0 + tok) * a.H + head) * D + g * DQ;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) qf[t] = ld16(qp + 8 * t);
+  } else {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) qf[t] = zero8();
+  }
+
+  const int64_t row_elems = (int64_t)a.Hkv * D;
+  const uint16_t* kbase = a.cache + (int64_t)it.kvh * D + g * DQ;
+  const int32_t* btrow = a.block_table + (int64_t)it.seq * a.bt_stride;
+  uint16_t* vl = smem + wave * 32 * VP;
+
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4_t o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int kb = kv0 + wave * 32; kb < kv1; kb += 4 * 32) {
+    bf16x8_t k0[NT], k1[NT], v0[NT], v1[NT];
+    const int key0 = kb + n, key1 = kb + 16 + n;
+    if (key0 < kv1) {
+      const int phys = btrow[key0 / a.BS];
+      const uint16_t* p = kbase + ((int64_t)phys * a.BS + key0 % a.BS) * row_elems;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) { k0[t] = ld16(p + 8 * t); v0[t] = ld16(p + a.plane + 8 * t); }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) { k0[t] = zero8(); v0[t] = zero8(); }
+    }
+    if (key1 < kv1) {
+      const int phys = btrow[key1 / a.BS];
+      const uint16_t* p = kbase + ((int64_t)phys * a.BS + key1 % a.BS) * row_elems;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) { k1[t] = ld16(p + 8 * t); v1[t] = ld16(p + a.plane + 8 * t); }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) { k1[t] = zero8(); v1[t] = zero8(); }
+    }
+    // stage V rows [key][d] of this step in the wave's LDS tile
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      *reinterpret_cast<bf16x8_t*>(vl + n * VP + g * DQ + 8 * t) = v0[t];
+      *reinterpret_cast<bf16x8_t*>(vl + (16 + n) * VP + g * DQ + 8 * t) = v1[t];
+    }
+    // S^T tiles: lane (n, g) reg i <- score of key kb + 4g + i (s0) and
+    // kb + 16 + 4g + i (s1) for row n
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0[t], qf[t], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[t], qf[t], s1, 0, 0, 0);
+    }
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = s0[i] * a.scale_log2;
+      x[4 + i] = s1[i] * a.scale_log2;
+    }
+    // tail and causal mask (cheap next to the loads, so always applied)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ka = kb + 4 * g + i, kc = kb + 16 + 4 * g + i;
+      if (ka >= kv1 || ka > row_limit) x[i] = kNegInf;
+      if (kc >= kv1 || kc > row_limit) x[4 + i] = kNegInf;
+    }
+    float mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+    mx = wave_max_xor(mx, 16);
+    mx = wave_max_xor(mx, 32);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float p[8], ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
+      ps += p[i];
+    }
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+    const bf16x8_t pb = pack_bf16x8(p);
+    // O^T += V^T P^T: A operand = 16 d x 32 keys read transposed from LDS;
+    // slots 0-3 hold keys 4g..4g+3, slots 4-7 keys 16+4g..16+4g+3, which is
+    // where the S^T layout left this lane's probabilities
+    const uint16_t* vr0 = vl + (4 * g + (n >> 2)) * VP + 4 * (n & 3);
+    const uint16_t* vr1 = vr0 + 16 * VP;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const bf16x8_t av = cat(lds_read_tr(vr0 + 16 * dt), lds_read_tr(vr1 + 16 * dt));
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, o[dt], 0, 0, 0);
+    }
+  }
+
+  // ---- merge the four waves' partial states through LDS
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  __syncthreads();
+  float* so = reinterpret_cast<float*>(smem_raw);
+  float* sm = so + 4 * 16 * D;
+  float* sl = sm + 64;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) so[(wave * 16 + n) * D + 16 * dt + 4 * g + i] = o[dt][i];
+  if (g == 0) {
+    sm[wave * 16 + n] = m_run;
+    sl[wave * 16 + n] = l_run;
+  }
+  __syncthreads();
+  constexpr int DPT = D / 16;  // d elements per thread in the epilogue
+  const int er = tid >> 4, ec = tid & 15;
+  if (er < nrows) {
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w * 16 + er]);
+    float wt[4], L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = sm[w * 16 + er];
+      wt[w] = (M == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      L += wt[w] * sl[w * 16 + er];
+    }
+    const bool empty = !(L > 0.f);
+    const float inv = empty ? 0.f : 1.f / L;
+    const float lse_v = empty ? kNegInf : (M + __log2f(L)) * kLn2;
+    float acc[DPT];
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) s += wt[w] * so[(w * 16 + er) * D + ec * DPT + e];
+      acc[e] = s * inv;
+    }
+    const int rr = it.row0 + er;
+    const int etok = rr / G;
+    const int ehead = it.kvh * G + (rr - etok * G);
+    if (it.prow < 0) {
+      const int64_t orow = (int64_t)(t0 + etok) * a.H + ehead;
+      uint16_t* op = a.out + orow * D + ec * DPT;
+      if constexpr (DPT % 8 == 0) {
+#pragma unroll
+        for (int e = 0; e < DPT; e += 8) *reinterpret_cast<bf16x8_t*>(op + e) = pack_bf16x8(acc + e);
+      } else {
+        static_assert(DPT == 4, "epilogue store");
+        uint2 w;
+        w.x = pack_bf16x2(acc[0], acc[1]);
+        w.y = pack_bf16x2(acc[2], acc[3]);
+        *reinterpret_cast<uint2*>(op) = w;
+      }
+      if (ec == 0 && a.lse) a.lse[orow] = lse_v;
+    } else {
+      float* pp = a.part_o + (int64_t)(it.prow + er) * D + ec * DPT;
+#pragma unroll
+      for (int e = 0; e < DPT; e += 4)
+        *reinterpret_cast<f32x4_t*>(pp + e) = f32x4_t{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+      if (ec == 0) a.part_lse[it.prow + er] = lse_v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Tiled attention: one workgroup of 4 waves per 128-row block; wave w owns
+// rows 32w..32w+31 (lane (n = lane%32, h = lane/32) owns row n and the key
+// half h of each 32x32 MFMA tile).  Key tiles of 64 keys are gathered
+// through the block table by all 256 threads into registers one tile ahead,
+// then stored to LDS (K with pitch D+8, V with pitch D+16 elements).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attn_tiled_kernel(AttnArgs a) {
+  constexpr int NKT = D / 16;       // QK k-steps (16 d each)
+  constexpr int NDT = D / 32;       // 32-wide d tiles of O^T
+  constexpr int KP = D + 8;
+  constexpr int VP = D + 16;
+  constexpr int CPR = D / 8;        // 16-byte chunks per key row
+  constexpr int LOADS = 64 * CPR / 256;
+  static_assert(LOADS >= 1, "tile loader");
+  __shared__ __attribute__((aligned(16))) uint16_t kl[64 * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t vl[64 * VP];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, h = lane >> 5;
+  const Item it = load_item(a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS);
+  const int t0 = a.cu[it.seq];
+  const int Lq = a.cu[it.seq + 1] - t0;
+  const int Lk = a.seqused_k[it.seq];
+  const int G = a.G;
+  const int nrows = min(it.nrows, Lq * G - it.row0);
+  const int kv1 = min(min(it.kv1, Lk), a.MB * a.BS);
+
+  const int rl = wave * 32 + n;
+  const int r = it.row0 + rl;
+  const bool row_ok = rl < nrows;
+  const int tok = r / G;
+  const int head = it.kvh * G + (r - tok * G);
+  const int row_limit = a.causal ? tok + Lk - Lq : INT_MAX;
+  // every row of this wave sees keys up to at least wave_limit
+  const int wave_limit = a.causal ? (it.row0 + wave * 32) / G + Lk - Lq : INT_MAX;
+
+  bf16x8_t qf[NKT];
+  if (row_ok) {
+    const uint16_t* qp = a.q + ((int64_t)(t0 + tok) * a.H + head) * D + 8 * h;
+#pragma unroll
+    for (int t = 0; t < NKT; ++t) qf[t] = ld16(qp + 16 * t);
+  } else {
+#pragma unroll
+    for (int t = 0; t < NKT; ++t) qf[t] = zero8();
+  }
+
+  const int64_t row_elems = (int64_t)a.Hkv * D;
+  const uint16_t* cbase = a.cache + (int64_t)it.kvh * D;
+  const int32_t* btrow = a.block_table + (int64_t)it.seq * a.bt_stride;
+
+  bf16x8_t kr[LOADS], vr[LOADS];
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int c = tid + 256 * i;
+      const int key = j0 + c / CPR;
+      const int col = c % CPR;
+      if (key < kv1) {
+        const int phys = btrow[key / a.BS];
+        const uint16_t* p = cbase + ((int64_t)phys * a.BS + key % a.BS) * row_elems + col * 8;
+        kr[i] = ld16(p);
+        vr[i] = ld16(p + a.plane);
+      } else {
+        kr[i] = zero8();
+        vr[i] = zero8();
+      }
+    }
+  };
+
+  float m_run = kNegInf, l_run = 0.f;
+  f32x16_t o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+
+  int j0 = it.kv0;
+  if (j0 < kv1) load_tile(j0);
+  const int q16 = lane >> 4, s16 = lane & 15;
+  for (; j0 < kv1; j0 += 64) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int c = tid + 256 * i;
+      const int key = c / CPR, col = c % CPR;
+      *reinterpret_cast<bf16x8_t*>(kl + key * KP + col * 8) = kr[i];
+      *reinterpret_cast<bf16x8_t*>(vl + key * VP + col * 8) = vr[i];
+    }
+    __syncthreads();
+    if (j0 + 64 < kv1) load_tile(j0 + 64);
+
+    // S^T: two 32-key tiles; lane (n, h) reg i <- key j0 + 32u + 8(i/4) + 4h + i%4
+    f32x16_t s[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[u][i] = 0.f;
+      const uint16_t* kp = kl + (32 * u + n) * KP + 8 * h;
+#pragma unroll
+      for (int t = 0; t < NKT; ++t) {
+        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kp + 16 * t);
+        s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[t], s[u], 0, 0, 0);
+      }
+    }
+    float x[32];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[16 * u + i] = s[u][i] * a.scale_log2;
+    if (j0 + 64 > kv1 || j0 + 63 > wave_limit) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = j0 + 32 * u + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (key >= kv1 || key > row_limit) x[16 * u + i] = kNegInf;
+        }
+    }
+    float mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, x[i]);
+    mx = wave_max_xor(mx, 32);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      x[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
+      ps += x[i];
+    }
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+    // P^T operands for the four 16-key steps: step ks = 2u + half uses
+    // regs 8*half .. 8*half+7 of tile u
+    bf16x8_t pb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) pb[ks] = pack_bf16x8(x + 8 * ks);
+    // O^T += V^T P^T; A operand lane (m = d row, h) slots: keys kb+4h+0..3,
+    // kb+8+4h+0..3 with kb = 16*ks, read transposed from LDS per 16-lane group
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint16_t* vr0 = vl + (16 * ks + 4 * h + (s16 >> 2)) * VP + 16 * (q16 & 1) + 4 * (s16 & 3);
+      const uint16_t* vr1 = vr0 + 8 * VP;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const bf16x8_t av = cat(lds_read_tr(vr0 + 32 * dt), lds_read_tr(vr1 + 32 * dt));
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks], o[dt], 0, 0, 0);
+      }
+    }
+  }
+
+  l_run += __shfl_xor(l_run, 32);
+  if (!row_ok) return;
+  const bool empty = !(l_run > 0.f);
+  const float inv = empty ? 0.f : 1.f / l_run;
+  const float lse_v = empty ? kNegInf : (m_run + __log2f(l_run)) * kLn2;
+  // lane (n, h) reg i of tile dt holds O^T[d = 32dt + 8(i/4) + 4h + i%4][row n]
+  if (it.prow < 0) {
+    const int64_t orow = (int64_t)(t0 + tok) * a.H + head;
+    uint16_t* op = a.out + orow * D + 4 * h;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) {
+        uint2 w;
+        w.x = pack_bf16x2(o[dt][4 * ig] * inv, o[dt][4 * ig + 1] * inv);
+        w.y = pack_bf16x2(o[dt][4 * ig + 2] * inv, o[dt][4 * ig + 3] * inv);
+        *reinterpret_cast<uint2*>(op + 32 * dt + 8 * ig) = w;
+      }
+    if (h == 0 && a.lse) a.lse[orow] = lse_v;
+  } else {
+    float* pp = a.part_o + (int64_t)(it.prow + rl) * D + 4 * h;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig)
+        *reinterpret_cast<f32x4_t*>(pp + 32 * dt + 8 * ig) =
+            f32x4_t{o[dt][4 * ig] * inv, o[dt][4 * ig + 1] * inv, o[dt][4 * ig + 2] * inv,
+                    o[dt][4 * ig + 3] * inv};
+    if (h == 0) a.part_lse[it.prow + rl] = lse_v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-KV reduction: one workgroup per reduce item, one wave per row.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void split_reduce_kernel(
+    const int32_t* __restrict__ ritems, const float* __restrict__ part_o,
+    const float* __restrict__ part_lse, const int32_t* __restrict__ cu, uint16_t* __restrict__ out,
+    float* __restrict__ lse, int H, int G) {
+  constexpr int EPL = D / 64;
+  static_assert(EPL >= 1, "split reduce");
+  const int32_t* p = ritems + (int64_t)blockIdx.x * PA_ITEM_WORDS;
+  const int seq = p[0], kvh = p[1], row0 = p[2], prow_n = p[3], prow0 = p[4], nsplit = p[5];
+  const int t0 = cu[seq];
+  const int Lq = cu[seq + 1] - t0;
+  const int nrows = min(prow_n, Lq * G - row0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int row = wave; row < nrows; row += 4) {
+    float M = kNegInf;
+    for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, part_lse[prow0 + s * prow_n + row]);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) M = wave_max_xor(M, m);
+    float acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+    float L = 0.f;
+    if (M != kNegInf) {
+      for (int s = 0; s < nsplit; ++s) {
+        const int pr = prow0 + s * prow_n + row;
+        const float ls = part_lse[pr];
+        const float w = (ls == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((ls - M) * kLog2e);
+        L += w;
+        const float* src = part_o + (int64_t)pr * D + lane * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] += w * src[e];
+      }
+    }
+    const bool empty = !(L > 0.f);
+    const float inv = empty ? 0.f : 1.f / L;
+    const int rr = row0 + row;
+    const int tok = rr / G;
+    const int head = kvh * G + (rr - tok * G);
+    const int64_t orow = (int64_t)(t0 + tok) * H + head;
+    uint16_t* op = out + orow * D + lane * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; e += 2) {
+      if (EPL == 1) {
+        op[0] = (uint16_t)(pack_bf16x2(acc[0] * inv, 0.f) & 0xffffu);
+      } else {
+        *reinterpret_cast<uint32_t*>(op + e) = pack_bf16x2(acc[e] * inv, acc[e + 1] * inv);
+      }
+    }
+    if (lane == 0 && lse) lse[orow] = empty ? kNegInf : M + __logf(L);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Two-way merge of (out, lse) partial states; one thread per 8 elements.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void merge_states_kernel(
+    uint16_t* out, float* __restrict__ out_lse, const uint16_t* po, const float* __restrict__ pl,
+    const uint16_t* so, const float* __restrict__ sl, int64_t rows, int32_t chunks_per_row) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gid / chunks_per_row;
+  if (row >= rows) return;
+  const int c = (int)(gid - row * chunks_per_row);
+  const float lp = pl[row], ls = sl[row];
+  const float M = fmaxf(lp, ls);
+  const int64_t off = row * chunks_per_row * 8 + c * 8;
+  const uint4 wp = *reinterpret_cast<const uint4*>(po + off);
+  const uint4 ws = *reinterpret_cast<const uint4*>(so + off);
+  float res[8];
+  float lse_v;
+  if (M == kNegInf) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) res[e] = 0.f;
+    lse_v = kNegInf;
+  } else {
+    const float wa = (lp == kNegInf) ? 0.f : expf(lp - M);
+    const float wb = (ls == kNegInf) ? 0.f : expf(ls - M);
+    const float den = wa + wb;
+    const float ia = wa / den, ib = wb / den;
+    const uint32_t pw[4] = {wp.x, wp.y, wp.z, wp.w};
+    const uint32_t sw[4] = {ws.x, ws.y, ws.z, ws.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      res[2 * e] = ia * __uint_as_float(pw[e] << 16) + ib * __uint_as_float(sw[e] << 16);
+      res[2 * e + 1] = ia * __uint_as_float(pw[e] & 0xffff0000u) +
+                       ib * __uint_as_float(sw[e] & 0xffff0000u);
+    }
+    lse_v = M + logf(den);
+  }
+  *reinterpret_cast<bf16x8_t*>(out + off) = pack_bf16x8(res);
+  if (c == 0 && out_lse) out_lse[row] = lse_v;
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+template <int D>
+pa_status launch_fwd(const AttnArgs& base, const pa_plan_info* plan, const int32_t* worklist,
+                     hipStream_t stream) {
+  const int32_t* items = worklist + PA_WORKLIST_HEADER_WORDS;
+  AttnArgs a = base;
+  if (plan->num_small_items > 0) {
+    a.items = items;
+    hipLaunchKernelGGL(attn_small_kernel<D>, dim3(plan->num_small_items), dim3(256), 0, stream, a);
+  }
+  if (plan->num_tiled_items > 0) {
+    a.items = items + (int64_t)plan->num_small_items * PA_ITEM_WORDS;
+    hipLaunchKernelGGL(attn_tiled_kernel<D>, dim3(plan->num_tiled_items), dim3(256), 0, stream, a);
+  }
+  if (plan->num_reduce_items > 0) {
+    const int32_t* r =
+        items + (int64_t)(plan->num_small_items + plan->num_tiled_items) * PA_ITEM_WORDS;
+    hipLaunchKernelGGL(split_reduce_kernel<D>, dim3(plan->num_reduce_items), dim3(256), 0, stream,
+                       r, base.part_o, base.part_lse, base.cu, base.out, base.lse, base.H, base.G);
+  }
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_reshape_and_cache(const void* key, const void* value, int64_t key_row_stride,
+                               int64_t value_row_stride, void* kv_cache,
+                               const int64_t* slot_mapping, int32_t num_tokens,
+                               int32_t num_kv_heads, int32_t head_size, int32_t num_blocks,
+                               int32_t block_size, hipStream_t stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_size <= 0 || head_size % 8 != 0 ||
+      head_size > 4096 || num_blocks <= 0 || block_size <= 0 || block_size % 16 != 0)
+    return PA_ERR_INVALID_ARGUMENT;
+  const int64_t row = (int64_t)num_kv_heads * head_size;
+  if (key_row_stride < row || value_row_stride < row || key_row_stride % 8 != 0 ||
+      value_row_stride % 8 != 0)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !kv_cache || !slot_mapping) return PA_ERR_INVALID_ARGUMENT;
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(kv_cache, 16) || !aligned(slot_mapping, 8))
+    return PA_ERR_INVALID_ARGUMENT;
+  const int64_t plane = (int64_t)num_blocks * block_size * row;
+  const int32_t cpr = (int32_t)(row / 8);
+  const int64_t total = (int64_t)num_tokens * 2 * cpr;
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks > INT32_MAX) return PA_ERR_INVALID_ARGUMENT;
+  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),
+                     key_row_stride, value_row_stride, static_cast<uint16_t*>(kv_cache),
+                     slot_mapping, total, cpr, row, plane);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_varlen_fwd(const pa_attn_params* p, const pa_plan_info* plan, const int32_t* worklist,
+                        const void* q, const void* kv_cache, const int32_t* cu_seqlens_q,
+                        const int32_t* seqused_k, const int32_t* block_table, int32_t num_tokens,
+                        void* out, float* lse, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  pa_status st = pa::check_params(p);
+  if (st != PA_OK) return st;
+  if (!plan) return PA_ERR_INVALID_ARGUMENT;
+  if (plan->batch != p->batch || plan->num_heads != p->num_heads ||
+      plan->num_kv_heads != p->num_kv_heads || plan->head_size != p->head_size ||
+      plan->causal != p->causal || plan->num_tokens != num_tokens)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (plan->num_small_items < 0 || plan->num_tiled_items < 0 || plan->num_reduce_items < 0 ||
+      plan->num_partial_rows < 0)
+    return PA_ERR_INVALID_ARGUMENT;
+  const int64_t n_items =
+      (int64_t)plan->num_small_items + plan->num_tiled_items + plan->num_reduce_items;
+  if (plan->worklist_bytes != (size_t)(PA_WORKLIST_HEADER_WORDS + n_items * PA_ITEM_WORDS) * 4)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < plan->workspace_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
+  if (plan->workspace_bytes > 0 && (!workspace || !aligned(workspace, 256)))
+    return PA_ERR_INVALID_ARGUMENT;
+  if (n_items == 0) return PA_OK;
+  if (!worklist || !q || !kv_cache || !cu_seqlens_q || !seqused_k || !block_table || !out)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(worklist, 4) ||
+      (lse && !aligned(lse, 4)))
+    return PA_ERR_INVALID_ARGUMENT;
+  if (plan->num_small_items > 0 && p->num_heads / p->num_kv_heads > PA_SMALL_MAX_ROWS)
+    return PA_ERR_INVALID_ARGUMENT;
+  AttnArgs a;
+  a.items = nullptr;
+  a.q = static_cast<const uint16_t*>(q);
+  a.cache = static_cast<const uint16_t*>(kv_cache);
+  a.cu = cu_seqlens_q;
+  a.seqused_k = seqused_k;
+  a.block_table = block_table;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  const size_t o_bytes = (size_t)plan->num_partial_rows * p->head_size * sizeof(float);
+  a.part_o = static_cast<float*>(workspace);
+  a.part_lse = workspace ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                                    (o_bytes + 255) / 256 * 256)
+                         : nullptr;
+  a.plane = (int64_t)p->num_blocks * p->block_size * p->num_kv_heads * p->head_size;
+  a.H = p->num_heads;
+  a.Hkv = p->num_kv_heads;
+  a.G = p->num_heads / p->num_kv_heads;
+  a.BS = p->block_size;
+  a.MB = p->max_blocks_per_seq;
+  a.bt_stride = p->block_table_stride ? p->block_table_stride : p->max_blocks_per_seq;
+  a.causal = p->causal;
+  a.scale_log2 = p->scale * kLog2e;
+  switch (p->head_size) {
+    case 64: return launch_fwd<64>(a, plan, worklist, stream);
+    case 128: return launch_fwd<128>(a, plan, worklist, stream);
+    case 256: return launch_fwd<256>(a, plan, worklist, stream);
+  }
+  return PA_ERR_UNSUPPORTED;
+}
+
+pa_status pa_merge_attn_states(void* out, float* out_lse, const void* prefix_out,
+                               const float* prefix_lse, const void* suffix_out,
+                               const float* suffix_lse, int32_t num_tokens, int32_t num_heads,
+                               int32_t head_size, hipStream_t stream) {
+  if (num_tokens < 0 || num_heads <= 0 || head_size <= 0 || head_size % 8 != 0 || head_size > 512)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (num_tokens == 0) return PA_OK;
+  if (!out || !prefix_out || !prefix_lse || !suffix_out || !suffix_lse)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (!aligned(out, 16) || !aligned(prefix_out, 16) || !aligned(suffix_out, 16))
+    return PA_ERR_INVALID_ARGUMENT;
+  const int64_t rows = (int64_t)num_tokens * num_heads;
+  const int32_t cpr = head_size / 8;
+  const int64_t blocks = (rows * cpr + 255) / 256;
+  if (blocks > INT32_MAX) return PA_ERR_INVALID_ARGUMENT;
+  hipLaunchKernelGGL(merge_states_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
+                     static_cast<uint16_t*>(out), out_lse, static_cast<const uint16_t*>(prefix_out),
+                     prefix_lse, static_cast<const uint16_t*>(suffix_out), suffix_lse, rows, cpr);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // extern "C"

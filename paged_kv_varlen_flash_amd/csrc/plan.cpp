@@ -1,0 +1,278 @@
+// Host-side planner and argument checks for libpagedattn.
+//
+// The planner turns the host mirrors of cu_seqlens_q / seqused_k into a fixed
+// work list, the ahead-of-time schedule of "FlashAttention 在 vLLM 中的实现分析"
+// (section 7): which rows of which (sequence, KV head) each workgroup takes,
+// which key range, and where split-KV partials go.  Pure host code: no HIP
+// call is made here, so every check can run on a machine without a GPU.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "pagedattn.h"
+#include "plan_internal.h"
+
+namespace pa {
+
+bool head_size_supported(int32_t d) {
+  for (int i = 0; i < PA_NUM_HEAD_SIZES; ++i)
+    if (pa_supported_head_sizes[i] == d) return true;
+  return false;
+}
+
+pa_status check_params(const pa_attn_params* p) {
+  if (!p) return PA_ERR_INVALID_ARGUMENT;
+  if (p->batch < 0 || p->num_heads <= 0 || p->num_kv_heads <= 0) return PA_ERR_INVALID_ARGUMENT;
+  if (p->num_heads % p->num_kv_heads != 0) return PA_ERR_INVALID_ARGUMENT;
+  // the FlashAttention backend asks for a head size that is a multiple of 8
+  // and at most 256 ("AttentionBackend" page, 境界と失敗)
+  if (p->head_size <= 0 || p->head_size % 8 != 0 || p->head_size > 256)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (!head_size_supported(p->head_size)) return PA_ERR_UNSUPPORTED;
+  // block size must be a multiple of 16 (same page, and the FlashAttention
+  // page's get_kv_cache_shape raises on any other size)
+  if (p->block_size <= 0 || p->block_size % 16 != 0) return PA_ERR_INVALID_ARGUMENT;
+  if (p->num_blocks <= 0 || p->max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARGUMENT;
+  if (p->block_table_stride != 0 && p->block_table_stride < p->max_blocks_per_seq)
+    return PA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)p->max_blocks_per_seq * p->block_size > INT32_MAX / 2) return PA_ERR_INVALID_ARGUMENT;
+  if (p->causal != 0 && p->causal != 1) return PA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(p->scale)) return PA_ERR_INVALID_ARGUMENT;
+  // byte offsets into the cache must fit in 64 bits with room to spare, and
+  // every per-launch index the kernels form in 32 bits must fit
+  const int64_t plane = (int64_t)p->num_blocks * p->block_size * p->num_kv_heads * p->head_size;
+  if (plane <= 0 || plane > ((int64_t)1 << 40)) return PA_ERR_INVALID_ARGUMENT;
+  return PA_OK;
+}
+
+namespace {
+
+struct Unit {        // one (sequence, kv head, row block) with its visible key range
+  int32_t seq, kvh, row0, nrows, kv_end;
+  bool small;
+};
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
+               int32_t force_splits, int32_t* wl, size_t cap, pa_plan_info* info) {
+  pa_status st = check_params(p);
+  if (st != PA_OK) return st;
+  if (!info) return PA_ERR_INVALID_ARGUMENT;
+  if (p->batch > 0 && (!cu || !sk)) return PA_ERR_INVALID_ARGUMENT;
+  if (force_splits < 0) return PA_ERR_INVALID_ARGUMENT;
+  const int32_t B = p->batch, H = p->num_heads, Hkv = p->num_kv_heads;
+  const int32_t G = H / Hkv;
+  const int64_t max_k = (int64_t)p->max_blocks_per_seq * p->block_size;
+  if (B > 0 && cu[0] != 0) return PA_ERR_INVALID_ARGUMENT;
+  for (int32_t b = 0; b < B; ++b) {
+    if (cu[b + 1] < cu[b]) return PA_ERR_INVALID_ARGUMENT;
+    if (sk[b] < 0 || sk[b] > max_k) return PA_ERR_INVALID_ARGUMENT;
+    // rows of one sequence are indexed in 32 bits
+    if ((int64_t)(cu[b + 1] - cu[b]) * G > INT32_MAX / 2) return PA_ERR_INVALID_ARGUMENT;
+  }
+  const int32_t T = B > 0 ? cu[B] : 0;
+  if ((int64_t)T * H > INT32_MAX) return PA_ERR_INVALID_ARGUMENT;
+
+  // ---- units: (seq, kvh, row block) with their visible key range
+  std::vector<Unit> units;
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t Lq = cu[b + 1] - cu[b], Lk = sk[b];
+    if (Lq == 0) continue;
+    const int32_t R = Lq * G;
+    const bool small = R <= PA_SMALL_MAX_ROWS;
+    const int32_t rb = small ? R : PA_TILED_ROWS;
+    for (int32_t kvh = 0; kvh < Hkv; ++kvh)
+      for (int32_t r0 = 0; r0 < R; r0 += rb) {
+        const int32_t nr = std::min(rb, R - r0);
+        int64_t kv_end = Lk;
+        if (p->causal) {
+          // bottom-right alignment: the block's last query token i sees keys
+          // j <= i + Lk - Lq
+          const int64_t i_last = (r0 + nr - 1) / G;
+          kv_end = std::min<int64_t>(Lk, std::max<int64_t>(0, i_last + Lk - Lq + 1));
+        }
+        units.push_back(Unit{b, kvh, r0, nr, (int32_t)kv_end, small});
+      }
+  }
+
+  // ---- split-KV choice
+  // small-row kernel: a workgroup walks its range in steps of SMALL_WG_KEYS
+  // keys; tiled kernel: KEY_TILE keys per tile.  Ranges are cut on these.
+  int64_t small_keys = 0, tiled_keys = 0, n_tiled = 0, n_small = 0;
+  for (const Unit& u : units) {
+    if (u.small) { small_keys += u.kv_end; ++n_small; }
+    else { tiled_keys += u.kv_end; ++n_tiled; }
+  }
+  const int64_t target = PA_PLAN_TARGET_CUS;
+  int64_t small_chunk = 0, tiled_chunk = 0;
+  if (force_splits == 0) {
+    // small rows are bound by HBM: cut ranges so there are about
+    // SMALL_WGS_PER_CU workgroups per CU, but never under SMALL_MIN_CHUNK keys
+    const int64_t want = target * kSmallWgsPerCu;
+    small_chunk = std::max<int64_t>(kSmallMinChunk,
+                                    ceil_div(ceil_div(std::max<int64_t>(small_keys, 1), want),
+                                             kSmallChunkAlign) * kSmallChunkAlign);
+    // tiled rows: split only when there are too few blocks to fill the chip
+    if (n_tiled > 0 && n_tiled < target) {
+      const int64_t want_t = 2 * target;
+      tiled_chunk = std::max<int64_t>(kTiledMinChunk,
+                                      ceil_div(ceil_div(std::max<int64_t>(tiled_keys, 1), want_t),
+                                               kKeyTile) * kKeyTile);
+    }
+  }
+
+  struct Item { int32_t w[PA_ITEM_WORDS]; int64_t cost; };
+  std::vector<Item> small_items, tiled_items, reduce_items;
+  int64_t prow = 0;
+  for (const Unit& u : units) {
+    // planner-chosen cuts fall on whole steps of the kernel; forced splits
+    // (tests) only keep ranges a multiple of 16 keys so tiny inputs still split
+    const int64_t align = force_splits > 0 ? 16 : (u.small ? kSmallChunkAlign : kKeyTile);
+    int64_t nsplit = 1, chunk = u.kv_end;
+    if (u.kv_end > 0) {
+      if (force_splits > 0) {
+        chunk = ceil_div(ceil_div(u.kv_end, force_splits), align) * align;
+      } else {
+        const int64_t c = u.small ? small_chunk : tiled_chunk;
+        if (c > 0 && u.kv_end > c) {
+          // equal-sized pieces, each a multiple of the alignment
+          const int64_t n = ceil_div(u.kv_end, c);
+          chunk = ceil_div(ceil_div(u.kv_end, n), align) * align;
+        }
+      }
+      chunk = std::max<int64_t>(chunk, align);
+      nsplit = ceil_div(u.kv_end, chunk);
+    }
+    auto& dst = u.small ? small_items : tiled_items;
+    if (nsplit <= 1) {
+      Item it{{u.seq, u.kvh, u.row0, u.nrows, 0, u.kv_end, -1, 0}, (int64_t)u.kv_end * u.nrows};
+      dst.push_back(it);
+      continue;
+    }
+    const int64_t base = prow;
+    for (int64_t s = 0; s < nsplit; ++s) {
+      const int64_t k0 = s * chunk, k1 = std::min<int64_t>(u.kv_end, k0 + chunk);
+      Item it{{u.seq, u.kvh, u.row0, u.nrows, (int32_t)k0, (int32_t)k1,
+               (int32_t)(base + s * u.nrows), 0},
+              (k1 - k0) * u.nrows};
+      dst.push_back(it);
+    }
+    prow += nsplit * u.nrows;
+    if (prow > INT32_MAX / 2) return PA_ERR_INVALID_ARGUMENT;
+    reduce_items.push_back(Item{{u.seq, u.kvh, u.row0, u.nrows, (int32_t)base, (int32_t)nsplit, 0, 0}, 0});
+  }
+  // longest work first, so the tail of the launch is short items (stable:
+  // equal costs keep the (seq, kv head) order, which keeps a sequence's
+  // blocks close in time and their keys warm in L2)
+  auto by_cost = [](const Item& a, const Item& b) { return a.cost > b.cost; };
+  std::stable_sort(tiled_items.begin(), tiled_items.end(), by_cost);
+  std::stable_sort(small_items.begin(), small_items.end(), by_cost);
+
+  const size_t n_items = small_items.size() + tiled_items.size() + reduce_items.size();
+  const size_t words = PA_WORKLIST_HEADER_WORDS + n_items * PA_ITEM_WORDS;
+  info->num_small_items = (int32_t)small_items.size();
+  info->num_tiled_items = (int32_t)tiled_items.size();
+  info->num_reduce_items = (int32_t)reduce_items.size();
+  info->num_partial_rows = (int32_t)prow;
+  info->batch = B;
+  info->num_heads = H;
+  info->num_kv_heads = Hkv;
+  info->head_size = p->head_size;
+  info->causal = p->causal;
+  info->num_tokens = T;
+  info->worklist_bytes = words * sizeof(int32_t);
+  // partial rows: fp32 [prow, D] values, then fp32 [prow] lse, 256-B aligned
+  const size_t o_bytes = (size_t)prow * p->head_size * sizeof(float);
+  const size_t l_bytes = (size_t)prow * sizeof(float);
+  info->workspace_bytes = prow ? ((o_bytes + 255) / 256 * 256 + (l_bytes + 255) / 256 * 256) : 0;
+  if (!wl) return PA_OK;
+  if (cap < info->worklist_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
+  std::memset(wl, 0, PA_WORKLIST_HEADER_WORDS * sizeof(int32_t));
+  wl[0] = PA_WORKLIST_MAGIC;
+  wl[1] = PA_WORKLIST_VERSION;
+  wl[2] = info->num_small_items;
+  wl[3] = info->num_tiled_items;
+  wl[4] = info->num_reduce_items;
+  wl[5] = info->num_partial_rows;
+  wl[6] = G;
+  wl[7] = p->causal;
+  int32_t* dst = wl + PA_WORKLIST_HEADER_WORDS;
+  for (auto* v : {&small_items, &tiled_items, &reduce_items})
+    for (const Item& it : *v) {
+      std::memcpy(dst, it.w, sizeof(it.w));
+      dst += PA_ITEM_WORDS;
+    }
+  return PA_OK;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+const int32_t pa_supported_head_sizes[PA_NUM_HEAD_SIZES] = {64, 128, 256};
+
+const char* pa_status_str(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARGUMENT: return "PA_ERR_INVALID_ARGUMENT";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_WORKSPACE_TOO_SMALL: return "PA_ERR_WORKSPACE_TOO_SMALL";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+  }
+  return "PA_ERR_UNKNOWN";
+}
+
+int32_t pa_version(void) { return (1 << 16) | 0; }
+
+pa_status pa_plan_varlen(const pa_attn_params* p, const int32_t* host_cu_seqlens_q,
+                         const int32_t* host_seqused_k, int32_t force_splits,
+                         int32_t* host_worklist, size_t worklist_capacity_bytes,
+                         pa_plan_info* info) {
+  return pa::plan(p, host_cu_seqlens_q, host_seqused_k, force_splits, host_worklist,
+                  worklist_capacity_bytes, info);
+}
+
+pa_status pa_cascade_split(const pa_attn_params* p, int32_t common_prefix_len,
+                           const int32_t* cu, const int32_t* sk, pa_attn_params* prefix_p,
+                           pa_attn_params* suffix_p, int32_t* prefix_cu, int32_t* prefix_sk,
+                           int32_t* suffix_sk, int32_t* col0) {
+  pa_status st = pa::check_params(p);
+  if (st != PA_OK) return st;
+  if (!prefix_p || !suffix_p || !prefix_cu || !prefix_sk || !col0) return PA_ERR_INVALID_ARGUMENT;
+  if (p->batch > 0 && (!cu || !sk || !suffix_sk)) return PA_ERR_INVALID_ARGUMENT;
+  if (p->causal != 1) return PA_ERR_INVALID_ARGUMENT;
+  const int32_t BS = p->block_size;
+  if (common_prefix_len <= 0 || common_prefix_len % BS != 0) return PA_ERR_INVALID_ARGUMENT;
+  const int32_t nblk = common_prefix_len / BS;
+  if (nblk >= p->max_blocks_per_seq + 1) return PA_ERR_INVALID_ARGUMENT;
+  if (p->batch > 0 && cu[0] != 0) return PA_ERR_INVALID_ARGUMENT;
+  for (int32_t b = 0; b < p->batch; ++b) {
+    const int32_t Lq = cu[b + 1] - cu[b];
+    if (Lq < 0 || sk[b] < 0) return PA_ERR_INVALID_ARGUMENT;
+    // every query token of every sequence lies after the shared prefix
+    if ((int64_t)common_prefix_len > (int64_t)sk[b] - Lq) return PA_ERR_INVALID_ARGUMENT;
+  }
+  const int32_t stride = p->block_table_stride ? p->block_table_stride : p->max_blocks_per_seq;
+  const int32_t T = p->batch > 0 ? cu[p->batch] : 0;
+  *prefix_p = *p;
+  prefix_p->batch = 1;
+  prefix_p->max_blocks_per_seq = nblk;
+  prefix_p->block_table_stride = stride;
+  prefix_p->causal = 0;
+  *suffix_p = *p;
+  suffix_p->max_blocks_per_seq = std::max(1, p->max_blocks_per_seq - nblk);
+  suffix_p->block_table_stride = stride;
+  prefix_cu[0] = 0;
+  prefix_cu[1] = T;
+  prefix_sk[0] = common_prefix_len;
+  for (int32_t b = 0; b < p->batch; ++b) suffix_sk[b] = sk[b] - common_prefix_len;
+  *col0 = nblk;
+  return PA_OK;
+}
+
+}  // extern "C"

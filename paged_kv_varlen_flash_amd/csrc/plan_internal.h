@@ -1,0 +1,32 @@
+// Shared between the planner (plan.cpp) and the launchers (pagedattn.hip):
+// the tile geometry both sides must agree on.
+#ifndef PAGEDATTN_PLAN_INTERNAL_H_
+#define PAGEDATTN_PLAN_INTERNAL_H_
+
+#include <cstdint>
+
+#include "pagedattn.h"
+
+namespace pa {
+
+// tiled kernel: 4 waves x 32 rows, key tiles of kKeyTile keys
+constexpr int kTiledWaves = 4;
+constexpr int kKeyTile = 64;
+constexpr int kTiledMinChunk = 256;
+// small-row kernel: 4 waves, each takes 32-key steps
+constexpr int kSmallWaves = 4;
+constexpr int kSmallStep = 32;
+constexpr int kSmallChunkAlign = kSmallStep * kSmallWaves;  // one step of every wave
+constexpr int kSmallMinChunk = 256;
+constexpr int kSmallWgsPerCu = 4;
+
+static_assert(PA_TILED_ROWS == kTiledWaves * 32, "tiled row block");
+
+pa_status check_params(const pa_attn_params* p);
+bool head_size_supported(int32_t d);
+pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
+               int32_t force_splits, int32_t* wl, size_t cap, pa_plan_info* info);
+
+}  // namespace pa
+
+#endif  // PAGEDATTN_PLAN_INTERNAL_H_

@@ -1,0 +1,326 @@
+"""ctypes binding of libpagedattn (declared in include/pagedattn.h).
+
+The ``pa_*`` functions mirror the C entry points one to one and only
+marshal arguments: tensors become device pointers, the current torch
+stream becomes the HIP stream, C status codes become ``PaError``.  Every
+computation runs in the library's HIP kernels (or, for the planner, in its
+host C++).  There is no fallback: if ``libpagedattn.so`` is missing or a
+tensor is not on the GPU, the call raises.
+
+``VarlenPlan``/``plan_varlen``, ``varlen_fwd`` and ``cascade_fwd`` are
+conveniences over the same calls: they size and allocate the device work
+list and workspace with torch and upload the planner's output.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+
+PA_OK = 0
+PA_ERR_INVALID_ARGUMENT = 1
+PA_ERR_UNSUPPORTED = 2
+PA_ERR_WORKSPACE_TOO_SMALL = 3
+PA_ERR_HIP = 4
+PA_WORKLIST_MAGIC = 0x50414731
+PA_WORKLIST_HEADER_WORDS = 16
+PA_ITEM_WORDS = 8
+
+EXPORTED = ["pa_status_str", "pa_version", "pa_supported_head_sizes", "pa_plan_varlen",
+            "pa_cascade_split", "pa_reshape_and_cache", "pa_varlen_fwd", "pa_merge_attn_states"]
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, where: str = ""):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} ({status})")
+
+
+class AttnParams(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_size", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32), ("block_table_stride", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+    def __repr__(self):
+        return "AttnParams(" + ", ".join(f"{k}={getattr(self, k)}" for k, _ in self._fields_) + ")"
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("num_small_items", ctypes.c_int32), ("num_tiled_items", ctypes.c_int32),
+                ("num_reduce_items", ctypes.c_int32), ("num_partial_rows", ctypes.c_int32),
+                ("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_size", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
+                ("worklist_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32P = ctypes.POINTER(ctypes.c_int32)
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m paged_kv_varlen_flash_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.pa_status_str.restype = ctypes.c_char_p
+        L.pa_status_str.argtypes = [ctypes.c_int]
+        L.pa_version.restype = ctypes.c_int32
+        L.pa_plan_varlen.restype = ctypes.c_int
+        L.pa_plan_varlen.argtypes = [ctypes.POINTER(AttnParams), _I32P, _I32P, ctypes.c_int32,
+                                     _I32P, ctypes.c_size_t, ctypes.POINTER(PlanInfo)]
+        L.pa_cascade_split.restype = ctypes.c_int
+        L.pa_cascade_split.argtypes = [ctypes.POINTER(AttnParams), ctypes.c_int32, _I32P, _I32P,
+                                       ctypes.POINTER(AttnParams), ctypes.POINTER(AttnParams),
+                                       _I32P, _I32P, _I32P, _I32P]
+        L.pa_reshape_and_cache.restype = ctypes.c_int
+        L.pa_reshape_and_cache.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_int64, _P, _P,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_int32, _P]
+        L.pa_varlen_fwd.restype = ctypes.c_int
+        L.pa_varlen_fwd.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(PlanInfo), _P,
+                                    _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P,
+                                    ctypes.c_size_t, _P]
+        L.pa_merge_attn_states.restype = ctypes.c_int
+        L.pa_merge_attn_states.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, _P]
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().pa_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != PA_OK:
+        raise PaError(status, where)
+
+
+def supported_head_sizes():
+    arr = (ctypes.c_int32 * 3).in_dll(lib(), "pa_supported_head_sizes")
+    return list(arr)
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr_i32(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(_I32P)
+
+
+def make_params(batch, num_heads, num_kv_heads, head_size, block_size, num_blocks,
+                max_blocks_per_seq, causal, scale, block_table_stride=0) -> AttnParams:
+    return AttnParams(int(batch), int(num_heads), int(num_kv_heads), int(head_size),
+                      int(block_size), int(num_blocks), int(max_blocks_per_seq),
+                      int(block_table_stride), int(bool(causal)), float(np.float32(scale)))
+
+
+# --------------------------------------------------------------------------
+# one-to-one wrappers
+# --------------------------------------------------------------------------
+def pa_plan_varlen(params: AttnParams, host_cu_seqlens_q, host_seqused_k,
+                   force_splits: int = 0) -> Tuple[np.ndarray, PlanInfo]:
+    """Host-only planner; returns (int32 work list, PlanInfo)."""
+    cu = _i32(host_cu_seqlens_q)
+    sk = _i32(host_seqused_k)
+    info = PlanInfo()
+    st = lib().pa_plan_varlen(ctypes.byref(params), _ptr_i32(cu), _ptr_i32(sk), int(force_splits),
+                              None, 0, ctypes.byref(info))
+    _check(st, "pa_plan_varlen(size)")
+    wl = np.zeros(info.worklist_bytes // 4, dtype=np.int32)
+    st = lib().pa_plan_varlen(ctypes.byref(params), _ptr_i32(cu), _ptr_i32(sk), int(force_splits),
+                              _ptr_i32(wl), wl.nbytes, ctypes.byref(info))
+    _check(st, "pa_plan_varlen")
+    return wl, info
+
+
+def pa_cascade_split(params: AttnParams, common_prefix_len: int, host_cu_seqlens_q,
+                     host_seqused_k):
+    """Host-only cascade metadata: (prefix_params, suffix_params, prefix_cu,
+    prefix_seqused_k, suffix_seqused_k, block_table_col0)."""
+    cu = _i32(host_cu_seqlens_q)
+    sk = _i32(host_seqused_k)
+    pp, sp = AttnParams(), AttnParams()
+    pcu = np.zeros(2, np.int32)
+    psk = np.zeros(1, np.int32)
+    ssk = np.zeros(max(len(sk), 1), np.int32)
+    col0 = np.zeros(1, np.int32)
+    st = lib().pa_cascade_split(ctypes.byref(params), int(common_prefix_len), _ptr_i32(cu),
+                                _ptr_i32(sk), ctypes.byref(pp), ctypes.byref(sp), _ptr_i32(pcu),
+                                _ptr_i32(psk), _ptr_i32(ssk), _ptr_i32(col0))
+    _check(st, "pa_cascade_split")
+    return pp, sp, pcu, psk, ssk[:len(sk)], int(col0[0])
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, what, dtype=None):
+    import torch
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{what} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def pa_reshape_and_cache(key, value, kv_cache, slot_mapping, stream=None):
+    """key/value: bf16 [T, Hkv, D] (row stride may exceed Hkv*D); kv_cache:
+    bf16 [2, NB, BS, Hkv, D] contiguous; slot_mapping int64 [T]."""
+    import torch
+    T, Hkv, D = key.shape
+    if value.shape != key.shape or key.stride(2) != 1 or value.stride(2) != 1 \
+            or key.stride(1) != D or value.stride(1) != D:
+        raise ValueError("key/value must be [T, Hkv, D] with contiguous heads")
+    if not kv_cache.is_contiguous() or kv_cache.dim() != 5 or kv_cache.shape[0] != 2:
+        raise ValueError("kv_cache must be a contiguous (2, NB, BS, Hkv, D) tensor")
+    if slot_mapping.shape[0] != T:
+        raise ValueError("slot_mapping must have one entry per token")
+    st = lib().pa_reshape_and_cache(
+        _dev(key, "key", torch.bfloat16), _dev(value, "value", torch.bfloat16),
+        key.stride(0), value.stride(0), _dev(kv_cache, "kv_cache", torch.bfloat16),
+        _dev(slot_mapping, "slot_mapping", torch.int64), T, Hkv, D, kv_cache.shape[1],
+        kv_cache.shape[2], _stream(stream))
+    _check(st, "pa_reshape_and_cache")
+
+
+def pa_varlen_fwd(params: AttnParams, plan: PlanInfo, worklist, q, kv_cache, cu_seqlens_q,
+                  seqused_k, block_table, out, lse=None, workspace=None, stream=None):
+    import torch
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().pa_varlen_fwd(
+        ctypes.byref(params), ctypes.byref(plan), _dev(worklist, "worklist", torch.int32),
+        _dev(q, "q", torch.bfloat16), _dev(kv_cache, "kv_cache", torch.bfloat16),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(seqused_k, "seqused_k", torch.int32),
+        _dev(block_table, "block_table", torch.int32), int(q.shape[0]),
+        _dev(out, "out", torch.bfloat16), _dev(lse, "lse", torch.float32),
+        _dev(workspace, "workspace"), ws_bytes, _stream(stream))
+    _check(st, "pa_varlen_fwd")
+
+
+def pa_merge_attn_states(out, out_lse, prefix_out, prefix_lse, suffix_out, suffix_lse,
+                         stream=None):
+    import torch
+    T, H, D = prefix_out.shape
+    for t in (out, prefix_out, suffix_out):
+        if not t.is_contiguous() or tuple(t.shape) != (T, H, D):
+            raise ValueError("merge operands must be contiguous [T, H, D]")
+    for t in (prefix_lse, suffix_lse) + ((out_lse,) if out_lse is not None else ()):
+        if not t.is_contiguous() or tuple(t.shape) != (T, H):
+            raise ValueError("lse operands must be contiguous [T, H]")
+    st = lib().pa_merge_attn_states(
+        _dev(out, "out", torch.bfloat16), _dev(out_lse, "out_lse", torch.float32),
+        _dev(prefix_out, "prefix_out", torch.bfloat16), _dev(prefix_lse, "prefix_lse", torch.float32),
+        _dev(suffix_out, "suffix_out", torch.bfloat16), _dev(suffix_lse, "suffix_lse", torch.float32),
+        T, H, D, _stream(stream))
+    _check(st, "pa_merge_attn_states")
+
+
+# --------------------------------------------------------------------------
+# conveniences
+# --------------------------------------------------------------------------
+class VarlenPlan:
+    """A planned call: params, host + device work list, device workspace."""
+
+    def __init__(self, params: AttnParams, host_cu_seqlens_q, host_seqused_k,
+                 force_splits: int = 0, device=None):
+        import torch
+        self.params = params
+        self.host_worklist, self.info = pa_plan_varlen(params, host_cu_seqlens_q, host_seqused_k,
+                                                       force_splits)
+        device = device or torch.device("cuda")
+        self.worklist = torch.from_numpy(self.host_worklist).to(device)
+        nbytes = max(int(self.info.workspace_bytes), 0)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
+
+
+def plan_varlen(q_shape, kv_cache_shape, block_table_shape, host_cu_seqlens_q, host_seqused_k,
+                scale, causal, force_splits=0, block_table_stride=0) -> VarlenPlan:
+    T, H, D = q_shape
+    _, NB, BS, Hkv, D2 = kv_cache_shape
+    if D2 != D:
+        raise ValueError("head size of q and kv_cache differ")
+    B, MB = block_table_shape
+    p = make_params(B, H, Hkv, D, BS, NB, MB, causal, scale, block_table_stride)
+    return VarlenPlan(p, host_cu_seqlens_q, host_seqused_k, force_splits)
+
+
+def varlen_fwd(q, kv_cache, cu_seqlens_q, seqused_k, block_table, plan: VarlenPlan,
+               out=None, lse=None, stream=None):
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
+    pa_varlen_fwd(plan.params, plan.info, plan.worklist, q, kv_cache, cu_seqlens_q, seqused_k,
+                  block_table, out, lse, plan.workspace, stream)
+    return out, lse
+
+
+class CascadePlan:
+    """Both cascade passes planned, with their small device metadata."""
+
+    def __init__(self, q_shape, kv_cache_shape, block_table_shape, host_cu_seqlens_q,
+                 host_seqused_k, scale, common_prefix_len, force_splits=0):
+        import torch
+        T, H, D = q_shape
+        _, NB, BS, Hkv, _ = kv_cache_shape
+        B, MB = block_table_shape
+        full = make_params(B, H, Hkv, D, BS, NB, MB, True, scale)
+        pp, sp, pcu, psk, ssk, col0 = pa_cascade_split(full, common_prefix_len,
+                                                       host_cu_seqlens_q, host_seqused_k)
+        self.prefix = VarlenPlan(pp, pcu, psk, force_splits)
+        self.suffix = VarlenPlan(sp, host_cu_seqlens_q, ssk, force_splits)
+        dev = torch.device("cuda")
+        self.prefix_cu = torch.from_numpy(pcu).to(dev)
+        self.prefix_seqused_k = torch.from_numpy(psk).to(dev)
+        self.suffix_seqused_k = torch.from_numpy(ssk).to(dev)
+        self.col0 = col0
+
+
+def cascade_fwd(q, kv_cache, cu_seqlens_q, block_table, plan: CascadePlan, out=None, lse=None,
+                prefix_out=None, prefix_lse=None, suffix_out=None, suffix_lse=None, stream=None):
+    """Prefix pass + suffix pass + merge.  Returns (out, lse)."""
+    import torch
+    T, H, D = q.shape
+    dev = q.device
+    if prefix_out is None:
+        prefix_out = torch.empty_like(q)
+        suffix_out = torch.empty_like(q)
+        prefix_lse = torch.empty(T, H, dtype=torch.float32, device=dev)
+        suffix_lse = torch.empty(T, H, dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(T, H, dtype=torch.float32, device=dev)
+    if not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous")
+    pa_varlen_fwd(plan.prefix.params, plan.prefix.info, plan.prefix.worklist, q, kv_cache,
+                  plan.prefix_cu, plan.prefix_seqused_k, block_table, prefix_out, prefix_lse,
+                  plan.prefix.workspace, stream)
+    suffix_bt = block_table[:, plan.col0:]   # strided view: same row stride
+    pa_varlen_fwd(plan.suffix.params, plan.suffix.info, plan.suffix.worklist, q, kv_cache,
+                  cu_seqlens_q, plan.suffix_seqused_k, suffix_bt, suffix_out, suffix_lse,
+                  plan.suffix.workspace, stream)
+    pa_merge_attn_states(out, lse, prefix_out, prefix_lse, suffix_out, suffix_lse, stream)
+    return out, lse

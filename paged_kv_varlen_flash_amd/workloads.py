@@ -318,3 +318,29 @@ def sample_sequences(wl: Workload, n: int) -> List[int]:
     """A seeded choice of n distinct sequence indices (sorted)."""
     n = min(n, wl.B)
     return sorted(int(i) for i in _rng(wl.seed, _TAG_SAMPLE).choice(wl.B, size=n, replace=False))
+
+
+def to_device(wl: Workload, device="cuda") -> dict:
+    """Torch tensors of a materialised workload (bf16 via a bit-preserving
+    view of the uint16 patterns)."""
+    import torch
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+    return {
+        "q": bf16(wl.q), "key": bf16(wl.key), "value": bf16(wl.value),
+        "kv_cache": bf16(wl.kv_cache),
+        "slot_mapping": torch.from_numpy(np.ascontiguousarray(wl.slot_mapping, dtype=np.int64)).to(device),
+        "cu_seqlens_q": i32(wl.cu_seqlens_q), "seqused_k": i32(wl.k_lens),
+        "block_table": i32(wl.block_table),
+    }
+
+
+def bf16_tensor_bits(t) -> np.ndarray:
+    """Device/host bf16 tensor -> numpy uint16 bit patterns."""
+    import torch
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)

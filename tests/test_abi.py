@@ -1,0 +1,280 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, rejects invalid arguments on the host before any HIP call, and
+plans work lists that cover every (row, key) exactly once.  No kernel runs."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from paged_kv_varlen_flash_amd import ops, workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ops.LIB_PATH):
+        from paged_kv_varlen_flash_amd import build
+        build.build()
+    return ops.lib()
+
+
+def header_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    funcs = set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text))
+    vars_ = set(re.findall(r"extern\s+const\s+\w+\s+(pa_[a-z0-9_]+)\s*\[", text))
+    return funcs | vars_
+
+
+def test_exports_every_declared_symbol(L):
+    syms = header_symbols()
+    assert {"pa_plan_varlen", "pa_reshape_and_cache", "pa_varlen_fwd",
+            "pa_merge_attn_states"} <= syms
+    for s in syms:
+        assert hasattr(L, s), f"{s} declared in pagedattn.h but not exported"
+    assert sorted(syms) == sorted(ops.EXPORTED)
+
+
+def test_status_strings_and_version(L):
+    assert ops.status_str(0) == "PA_OK"
+    assert ops.status_str(3) == "PA_ERR_WORKSPACE_TOO_SMALL"
+    assert ops.status_str(99) == "PA_ERR_UNKNOWN"
+    assert L.pa_version() >> 16 == 1
+    assert ops.supported_head_sizes() == [64, 128, 256]
+
+
+def params(**kw):
+    base = dict(batch=2, num_heads=4, num_kv_heads=2, head_size=64, block_size=16,
+                num_blocks=16, max_blocks_per_seq=6, causal=True, scale=0.125)
+    raw_causal = kw.pop("raw_causal", None)
+    base.update(kw)
+    p = ops.make_params(**base)
+    if raw_causal is not None:
+        p.causal = raw_causal
+    return p
+
+
+CU = [0, 37, 38]
+SK = [37, 81]
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block_size=24), ops.PA_ERR_INVALID_ARGUMENT),      # not a multiple of 16
+    (dict(block_size=0), ops.PA_ERR_INVALID_ARGUMENT),
+    (dict(head_size=96), ops.PA_ERR_UNSUPPORTED),            # valid size, not compiled
+    (dict(head_size=100), ops.PA_ERR_INVALID_ARGUMENT),      # not a multiple of 8
+    (dict(head_size=512), ops.PA_ERR_INVALID_ARGUMENT),      # above 256
+    (dict(num_heads=5), ops.PA_ERR_INVALID_ARGUMENT),        # H % Hkv != 0
+    (dict(num_kv_heads=0), ops.PA_ERR_INVALID_ARGUMENT),
+    (dict(batch=-1), ops.PA_ERR_INVALID_ARGUMENT),
+    (dict(max_blocks_per_seq=5), ops.PA_ERR_INVALID_ARGUMENT),  # 81 keys need 6 blocks
+    (dict(raw_causal=2), ops.PA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("nan")), ops.PA_ERR_INVALID_ARGUMENT),
+    (dict(block_table_stride=3), ops.PA_ERR_INVALID_ARGUMENT),
+])
+def test_plan_rejects(L, kw, status):
+    with pytest.raises(ops.PaError) as e:
+        ops.pa_plan_varlen(params(**kw), CU, SK)
+    assert e.value.status == status
+
+
+def test_plan_rejects_bad_lengths(L):
+    with pytest.raises(ops.PaError):
+        ops.pa_plan_varlen(params(), [1, 37, 38], SK)          # cu[0] != 0
+    with pytest.raises(ops.PaError):
+        ops.pa_plan_varlen(params(), [0, 37, 30], SK)          # decreasing
+    with pytest.raises(ops.PaError):
+        ops.pa_plan_varlen(params(), CU, [37, -1])
+    with pytest.raises(ops.PaError):
+        ops.pa_plan_varlen(params(), CU, SK, force_splits=-2)
+
+
+def test_plan_capacity_error(L):
+    p = params()
+    info = ops.PlanInfo()
+    cu = np.array(CU, np.int32)
+    sk = np.array(SK, np.int32)
+    small = np.zeros(4, np.int32)
+    st = L.pa_plan_varlen(ctypes.byref(p), cu.ctypes.data_as(ops._I32P),
+                          sk.ctypes.data_as(ops._I32P), 0, small.ctypes.data_as(ops._I32P),
+                          small.nbytes, ctypes.byref(info))
+    assert st == ops.PA_ERR_WORKSPACE_TOO_SMALL
+    assert info.worklist_bytes > small.nbytes
+
+
+def _fwd_call(L, p, info, **override):
+    """pa_varlen_fwd with fake (never dereferenced) pointers; only calls that
+    fail host validation may be made on a machine without a GPU."""
+    args = dict(worklist=0x1000, q=0x2000, kv=0x3000, cu=0x4000, sk=0x5000, bt=0x6000,
+                T=info.num_tokens if info is not None else 38, out=0x7000, lse=0x8000, ws=0x10000, ws_bytes=1 << 30)
+    args.update(override)
+    P = ctypes.c_void_p
+    return L.pa_varlen_fwd(ctypes.byref(p), ctypes.byref(info) if info is not None else None,
+                           P(args["worklist"]), P(args["q"]), P(args["kv"]), P(args["cu"]),
+                           P(args["sk"]), P(args["bt"]), args["T"], P(args["out"]),
+                           P(args["lse"]), P(args["ws"]), args["ws_bytes"], None)
+
+
+def test_fwd_validation_before_launch(L):
+    p = params()
+    _, info = ops.pa_plan_varlen(p, CU, SK, force_splits=3)
+    assert info.workspace_bytes > 0
+    E = ops.PA_ERR_INVALID_ARGUMENT
+    assert _fwd_call(L, p, None) == E
+    assert _fwd_call(L, p, info, q=0) == E
+    assert _fwd_call(L, p, info, worklist=0) == E
+    assert _fwd_call(L, p, info, out=0) == E
+    assert _fwd_call(L, p, info, bt=0) == E
+    assert _fwd_call(L, p, info, q=0x2008) == E              # misaligned
+    assert _fwd_call(L, p, info, ws=0) == E
+    assert _fwd_call(L, p, info, ws=0x10010) == E            # not 256-B aligned
+    assert _fwd_call(L, p, info, T=info.num_tokens + 1) == E  # plan/params mismatch
+    assert _fwd_call(L, p, info, ws_bytes=info.workspace_bytes - 1) == ops.PA_ERR_WORKSPACE_TOO_SMALL
+    p2 = params(causal=False)
+    assert _fwd_call(L, p2, info) == E                       # planned causal, called non-causal
+    p3 = params(head_size=96)
+    assert _fwd_call(L, p3, info) == ops.PA_ERR_UNSUPPORTED
+
+
+def test_reshape_and_cache_validation(L):
+    P = ctypes.c_void_p
+    E = ops.PA_ERR_INVALID_ARGUMENT
+    ok = dict(k=0x1000, v=0x2000, ks=128, vs=128, c=0x3000, s=0x4000, T=4, Hkv=2, D=64, NB=4, BS=16)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.pa_reshape_and_cache(P(a["k"]), P(a["v"]), a["ks"], a["vs"], P(a["c"]), P(a["s"]),
+                                      a["T"], a["Hkv"], a["D"], a["NB"], a["BS"], None)
+    assert call(BS=24) == E
+    assert call(D=60) == E
+    assert call(ks=64) == E          # stride below Hkv*D
+    assert call(vs=130) == E         # stride not a multiple of 8
+    assert call(k=0) == E
+    assert call(s=0) == E
+    assert call(c=0x3004) == E       # misaligned cache
+    assert call(T=-1) == E
+    assert call(T=0, k=0, v=0, c=0, s=0) == ops.PA_OK   # nothing to do: no launch
+
+
+def test_merge_validation(L):
+    P = ctypes.c_void_p
+    E = ops.PA_ERR_INVALID_ARGUMENT
+    f = L.pa_merge_attn_states
+    assert f(P(0x1000), None, P(0x2000), P(0x3000), P(0x4000), P(0x5000), 4, 2, 60, None) == E
+    assert f(P(0x1000), None, P(0), P(0x3000), P(0x4000), P(0x5000), 4, 2, 64, None) == E
+    assert f(P(0x1008), None, P(0x2000), P(0x3000), P(0x4000), P(0x5000), 4, 2, 64, None) == E
+    assert f(P(0), None, P(0), P(0), P(0), P(0), 0, 2, 64, None) == ops.PA_OK
+
+
+def test_cascade_split(L):
+    wl = W.make("cascade_prefix", materialise=False)
+    p = ops.make_params(wl.B, wl.H, wl.Hkv, wl.D, wl.BS, wl.num_blocks, wl.block_table.shape[1],
+                        True, wl.scale)
+    pp, sp, pcu, psk, ssk, col0 = ops.pa_cascade_split(p, 2048, wl.cu_seqlens_q, wl.k_lens)
+    assert col0 == 2048 // 16 and list(pcu) == [0, wl.T] and list(psk) == [2048]
+    assert np.array_equal(ssk, wl.k_lens - 2048)
+    assert pp.batch == 1 and pp.causal == 0 and pp.max_blocks_per_seq == 128
+    assert sp.causal == 1 and sp.block_table_stride == wl.block_table.shape[1]
+    with pytest.raises(ops.PaError):
+        ops.pa_cascade_split(p, 2040, wl.cu_seqlens_q, wl.k_lens)     # not block aligned
+    with pytest.raises(ops.PaError):
+        ops.pa_cascade_split(p, 4096, wl.cu_seqlens_q, wl.k_lens)     # longer than a context
+
+
+# ---------------------------------------------------------------- plan coverage
+def parse(wl_words, info):
+    assert wl_words[0] == ops.PA_WORKLIST_MAGIC
+    n_att = info.num_small_items + info.num_tiled_items
+    items = wl_words[16:16 + 8 * n_att].reshape(-1, 8)
+    red = wl_words[16 + 8 * n_att:].reshape(-1, 8)
+    assert len(red) == info.num_reduce_items
+    return items, red
+
+
+def check_plan_covers(H, Hkv, q_lens, k_lens, causal, force_splits=0):
+    """Every visible (row, key) pair is covered by exactly one item; split
+    units have a reduce item whose partial rows match their items."""
+    G = H // Hkv
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    BS = 16
+    MB = max(1, max((k + BS - 1) // BS for k in k_lens))
+    p = ops.make_params(len(q_lens), H, Hkv, 64, BS, 4096, MB, causal, 0.1)
+    words, info = ops.pa_plan_varlen(p, cu, k_lens, force_splits)
+    items, red = parse(words, info)
+    cover = {}
+    small_rows = PA_SMALL = 16
+    for idx, (seq, kvh, row0, nrows, k0, k1, prow, _) in enumerate(items):
+        is_small = idx < info.num_small_items
+        assert nrows <= (PA_SMALL if is_small else 128) and nrows >= 1
+        for r in range(row0, row0 + nrows):
+            cover.setdefault((seq, kvh, r), []).append((k0, k1, prow))
+    seen_prow = set()
+    for b in range(len(q_lens)):
+        Lq, Lk = int(q_lens[b]), int(k_lens[b])
+        for kvh in range(Hkv):
+            for r in range(Lq * G):
+                ranges = sorted(cover.pop((b, kvh, r)))
+                i = r // G
+                vis_end = min(Lk, max(0, i + Lk - Lq + 1)) if causal else Lk
+                # ranges tile [0, end) with end >= vis_end, and nothing past Lk
+                pos = 0
+                for k0, k1, _ in ranges:
+                    assert k0 == pos
+                    pos = k1
+                assert pos >= vis_end and pos <= Lk
+                if len(ranges) > 1:
+                    for _, _, prow in ranges:
+                        assert prow >= 0
+                        seen_prow.add(prow)
+                else:
+                    assert ranges[0][2] == -1
+    assert not cover, "items for rows that do not exist"
+    # reduce items point at the split items' partial rows
+    for seq, kvh, row0, nrows, prow0, nsplit, _, _ in red:
+        assert nsplit >= 2
+        for s in range(nsplit):
+            assert prow0 + s * nrows in seen_prow
+    assert info.num_partial_rows == (max(seen_prow) + 1 if seen_prow else 0) or \
+        info.num_partial_rows >= len(seen_prow)
+    return info
+
+
+@pytest.mark.parametrize("force", [0, 1, 3, 7])
+def test_plan_covers_mixed(L, force):
+    rng = np.random.default_rng(force)
+    q_lens = np.array([37, 1, 1, 200, 3, 1, 0, 129], np.int32)
+    k_lens = np.array([37, 81, 1, 250, 40, 0, 5, 129], np.int32)
+    for causal in (True, False):
+        check_plan_covers(8, 2, q_lens, k_lens, causal, force)
+        check_plan_covers(4, 4, q_lens, k_lens, causal, force)
+    q2 = rng.integers(1, 40, size=12).astype(np.int32)
+    k2 = (q2 + rng.integers(0, 300, size=12)).astype(np.int32)
+    check_plan_covers(32, 8, q2, k2, True, force)
+
+
+@pytest.mark.parametrize("name", W.ORDER)
+def test_plan_covers_workloads(L, name):
+    wl = W.make(name, materialise=False)
+    if wl.T * wl.H > 5000 * 32:
+        # full coverage on the big mix is slow in Python; check the counts only
+        p = ops.make_params(wl.B, wl.H, wl.Hkv, wl.D, wl.BS, wl.num_blocks,
+                            wl.block_table.shape[1], wl.causal, wl.scale)
+        words, info = ops.pa_plan_varlen(p, wl.cu_seqlens_q, wl.k_lens)
+        items, red = parse(words, info)
+        assert info.num_tiled_items > 0 and info.num_small_items > 0
+        return
+    check_plan_covers(wl.H, wl.Hkv, wl.q_lens, wl.k_lens, wl.causal)
+
+
+def test_plan_is_deterministic(L):
+    wl = W.make("decode_llama8b", materialise=False)
+    p = ops.make_params(wl.B, wl.H, wl.Hkv, wl.D, wl.BS, wl.num_blocks, wl.block_table.shape[1],
+                        True, wl.scale)
+    a, _ = ops.pa_plan_varlen(p, wl.cu_seqlens_q, wl.k_lens)
+    b, _ = ops.pa_plan_varlen(p, wl.cu_seqlens_q, wl.k_lens)
+    assert np.array_equal(a, b)
