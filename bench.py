@@ -1,0 +1,274 @@
+"""Benchmark of the paged varlen attention path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--secondary]
+
+A step is one pass of the whole path over one batch that is already resident
+in HBM: the host planner (pa_plan_varlen, whose work list is copied to the
+device from pinned memory), pa_reshape_and_cache for the batch's new tokens,
+and pa_varlen_fwd (attention kernels + split-KV reduce); the cascade workload
+adds its two passes and pa_merge_attn_states.  The headline workload is the
+64-sequence Llama-3-8B-shaped decode batch.
+
+Printed: one JSON line with the whole-step throughput (algorithmic KV bytes
+per second), a roofline object for the attention call -- its algorithmic
+bytes (or flops) divided by its average duration, measured with HIP events
+on the launch stream over separate timed launches with the caches flushed
+in between -- and the fp64 oracle timed on the host cores on a bounded
+sample of the same workload.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_llama8b")
+    ap.add_argument("--kernel-reps", type=int, default=30)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget for the oracle CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--secondary", action="store_true",
+                    help="also time the prefill mix and the long-context decode")
+    return ap.parse_args()
+
+
+class Step:
+    """Everything one step needs, resident on the GPU."""
+
+    def __init__(self, wl, dev):
+        import torch
+        from paged_kv_varlen_flash_amd import ops, workloads as W
+        self.ops, self.wl = ops, wl
+        self.d = W.to_device(wl, dev)
+        d = self.d
+        self.params = ops.make_params(wl.B, wl.H, wl.Hkv, wl.D, wl.BS, wl.num_blocks,
+                                      wl.block_table.shape[1], wl.causal, wl.scale)
+        self.cu = np.ascontiguousarray(wl.cu_seqlens_q, np.int32)
+        self.sk = np.ascontiguousarray(wl.k_lens, np.int32)
+        words, info = ops.pa_plan_varlen(self.params, self.cu, self.sk)
+        self.cap = words.nbytes
+        # two pinned host buffers: the plan of step t is written while the copy
+        # of step t-1 may still be queued
+        self.pinned = [torch.empty(words.size, dtype=torch.int32).pin_memory() for _ in range(2)]
+        self.copy_done = [None, None]
+        self.worklist = torch.from_numpy(words).to(dev)
+        self.info = info
+        self.workspace = torch.empty(max(info.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+        self.out = torch.empty_like(d["q"])
+        self.lse = torch.empty(wl.T, wl.H, dtype=torch.float32, device=dev)
+        self.i = 0
+        self.cascade = None
+        if wl.spec.shared_prefix:
+            self.cascade = ops.CascadePlan(tuple(d["q"].shape), tuple(d["kv_cache"].shape),
+                                           tuple(d["block_table"].shape), wl.cu_seqlens_q,
+                                           wl.k_lens, wl.scale, wl.spec.shared_prefix)
+            self.parts = [torch.empty_like(self.out), torch.empty_like(self.lse),
+                          torch.empty_like(self.out), torch.empty_like(self.lse)]
+
+    def plan(self):
+        import torch
+        ops = self.ops
+        k = self.i & 1
+        self.i += 1
+        if self.copy_done[k] is not None:
+            self.copy_done[k].synchronize()
+        buf = self.pinned[k]
+        info = ops.PlanInfo()
+        st = ops.lib().pa_plan_varlen(ctypes.byref(self.params),
+                                      self.cu.ctypes.data_as(ops._I32P),
+                                      self.sk.ctypes.data_as(ops._I32P), 0,
+                                      ctypes.cast(buf.data_ptr(), ops._I32P), self.cap,
+                                      ctypes.byref(info))
+        if st != 0:
+            raise ops.PaError(st, "pa_plan_varlen")
+        self.worklist.copy_(buf, non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self.copy_done[k] = ev
+        self.info = info
+
+    def scatter(self):
+        d = self.d
+        self.ops.pa_reshape_and_cache(d["key"], d["value"], d["kv_cache"], d["slot_mapping"])
+
+    def attention(self):
+        d, ops = self.d, self.ops
+        if self.cascade is None:
+            ops.pa_varlen_fwd(self.params, self.info, self.worklist, d["q"], d["kv_cache"],
+                              d["cu_seqlens_q"], d["seqused_k"], d["block_table"], self.out,
+                              self.lse, self.workspace)
+        else:
+            ops.cascade_fwd(d["q"], d["kv_cache"], d["cu_seqlens_q"], d["block_table"],
+                            self.cascade, out=self.out, lse=self.lse,
+                            prefix_out=self.parts[0], prefix_lse=self.parts[1],
+                            suffix_out=self.parts[2], suffix_lse=self.parts[3])
+
+    def __call__(self):
+        if self.cascade is None:
+            self.plan()
+        self.scatter()
+        self.attention()
+
+
+def time_steps(step, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def time_attention(step, reps, flush):
+    """Average duration of the attention call, HIP events on its stream, with
+    a cache-flushing write between launches (outside the timed interval)."""
+    import torch
+    s = torch.cuda.current_stream()
+    times = []
+    for _ in range(reps):
+        flush.fill_(1)
+        # a short spin keeps the GPU busy while the host enqueues the call, so
+        # the interval below holds device time only
+        torch.cuda._sleep(400000)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        step.attention()
+        e1.record(s)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3)
+    times = np.array(times)
+    return float(times.mean()), float(np.median(times))
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def cpu_baseline(wl, budget_s):
+    """The fp64 oracle (as it stands) on whole sequences of the same batch
+    until the time budget is used; KV-read GB/s over the sequences done."""
+    import oracle.attention as OA
+    cache = OA.reshape_and_cache(wl.key, wl.value, wl.kv_cache, wl.slot_mapping)
+    done, nbytes = 0, 0
+    t0 = time.perf_counter()
+    # whole sequences, cycling through the batch, until the budget is spent
+    while time.perf_counter() - t0 < budget_s:
+        b = done % wl.B
+        t_a, t_b = int(wl.cu_seqlens_q[b]), int(wl.cu_seqlens_q[b + 1])
+        OA.varlen_attention(wl.q[t_a:t_b], cache, np.array([0, t_b - t_a]), wl.k_lens[b:b + 1],
+                            wl.block_table[b:b + 1], wl.scale, wl.causal)
+        nbytes += 2 * int(wl.k_lens[b]) * wl.Hkv * wl.D * 2
+        done += 1
+    el = time.perf_counter() - t0
+    return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"{done} sequence passes over the {wl.B} sequences of {wl.spec.name} "
+                      f"({nbytes/1e6:.1f} MB of KV), fp64 numpy, {el:.1f} s wall"}
+
+
+def measure(name, args, dev, flush, with_cpu):
+    import torch
+    from paged_kv_varlen_flash_amd import workloads as W
+    wl = W.make(name)
+    step = Step(wl, dev)
+    per_step = time_steps(step, args.steps, args.warmup)
+    t_mean, t_med = time_attention(step, args.kernel_reps, flush)
+    kv = wl.kv_read_bytes()
+    flops = wl.attention_flops()
+    res = {"workload": name, "wl": wl, "ms_per_step": per_step * 1e3, "attn_mean_s": t_mean,
+           "attn_median_s": t_med, "kv_bytes": kv, "flops": flops, "plan": step.info.as_dict()}
+    if with_cpu:
+        res["cpu"] = cpu_baseline(wl, args.cpu_seconds)
+    del step
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from paged_kv_varlen_flash_amd import ops
+    if not os.path.exists(ops.LIB_PATH):
+        raise SystemExit("libpagedattn.so is not built: python -m paged_kv_varlen_flash_amd.build")
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    head = measure(args.workload, args, dev, flush, not args.no_cpu_baseline)
+    wl = head["wl"]
+    decode_like = wl.q_lens.max() * (wl.H // wl.Hkv) <= 16 or args.workload == "cascade_prefix"
+    value = head["kv_bytes"] / (head["ms_per_step"] * 1e-3) / 1e9
+    if decode_like:
+        ach = head["kv_bytes"] / head["attn_mean_s"] / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "pa_varlen_fwd (attn_small_kernel<%d> + split_reduce_kernel<%d>)"
+                          % (wl.D, wl.D),
+                "per_launch_bytes": head["kv_bytes"],
+                "avg_launch_us": round(head["attn_mean_s"] * 1e6, 2),
+                "median_launch_us": round(head["attn_median_s"] * 1e6, 2)}
+    else:
+        ach = head["flops"] / head["attn_mean_s"] / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "pa_varlen_fwd", "per_launch_flops": head["flops"],
+                "avg_launch_us": round(head["attn_mean_s"] * 1e6, 2)}
+    line = {
+        "metric": "decode KV-read GB/s (HBM roofline fraction in roofline.frac)",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, shuffled physical blocks)",
+        "config": dict(wl.summary(), parallelism="none (1 GPU)"),
+        "roofline": roof,
+    }
+    if "cpu" in head:
+        line["cpu_baseline"] = head["cpu"]
+    if args.secondary:
+        sec = {}
+        for name in ("chunked_prefill_mix", "long_decode_d256", "cascade_prefix"):
+            r = measure(name, args, dev, flush, False)
+            w = r["wl"]
+            ent = {"ms_per_step": round(r["ms_per_step"], 4),
+                   "attn_avg_us": round(r["attn_mean_s"] * 1e6, 2),
+                   "kv_GBps": round(r["kv_bytes"] / r["attn_mean_s"] / 1e9, 1),
+                   "hbm_frac": round(r["kv_bytes"] / r["attn_mean_s"] / 1e9 / HBM_PEAK_GBS, 4)}
+            if name == "chunked_prefill_mix":
+                ent["attn_TFLOPs"] = round(r["flops"] / r["attn_mean_s"] / 1e12, 1)
+                ent["mfma_frac"] = round(r["flops"] / r["attn_mean_s"] / 1e12 / BF16_PEAK_TFLOPS, 4)
+            sec[name] = ent
+        line["secondary"] = sec
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -110,6 +110,7 @@ typedef struct {
   int32_t num_tiled_items;   /* items for the 128-row tiled kernel           */
   int32_t num_reduce_items;  /* split-KV merges                              */
   int32_t num_partial_rows;  /* fp32 partial rows held in the workspace      */
+  int32_t max_reduce_rows;   /* most rows of any reduce item                 */
   int32_t batch, num_heads, num_kv_heads, head_size, causal, num_tokens;
   size_t worklist_bytes;
   size_t workspace_bytes;

@@ -137,25 +137,51 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Small-row attention: one workgroup of 4 waves per work item of <= 16 rows.
-// Each wave takes 32-key steps (wave w: keys kv0 + 32*(w + 4i) ...), so a
-// step is 2 MFMA tiles of 16 keys.  Lane (n = lane%16, g = lane/16) owns
-// query row n; for the QK^T product it loads K row (step + n) and
-// (step + 16 + n), d range [g*D/4, (g+1)*D/4), straight from the cache into
-// registers (the MFMA A operand), and the V rows of the same keys, which it
-// stages in its wave's LDS tile for the transposing read.
+// Small-row attention: one workgroup of 4 waves per work item of <= 16 rows
+// (decode: the G query heads of one KV head, times at most 16/G tokens).
+// The item's key range is walked in 16-key steps; wave w takes steps w,
+// w+4, w+8, ...  K and V are read once, so the kernel is bound by HBM:
+//   * loads are non-temporal and coalesced: CPR = D/8 consecutive lanes read
+//     one key row (D*2 contiguous bytes) 16 bytes each, so every wave
+//     instruction covers 64/CPR whole rows;
+//   * each wave keeps PF steps of loads in flight in registers, and stages
+//     the step it computes in a private LDS tile (K and V, [16][D]) whose
+//     16-byte chunks are XOR-swizzled by row so that the MFMA operand reads
+//     (four lanes per row for K, a transposing read for V) avoid bank
+//     conflicts.
+// Lane (n = lane%16, g = lane/16) owns query row n: S^T = K Q^T on
+// 16x16x32 MFMA (k-step t: d chunk 4t+g), O^T = V^T P^T on 16x16x16 MFMA
+// (P^T slots = keys 4g..4g+3, exactly where the S^T layout left them).
+// Item key ranges start on a multiple of 16, and block_size is a multiple
+// of 16, so the 16 keys of a step lie in one cache block.
 // ---------------------------------------------------------------------------
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct SmallCfg {
+  static constexpr int CPR = D / 8;          // 16-byte chunks per key row
+  static constexpr int LPR = 64 / CPR;       // key rows per wave load instruction
+  static constexpr int NLD = 16 / LPR;       // load instructions per plane per step
+  static constexpr int PF = (D == 256) ? 2 : 3;  // steps of loads in flight
+  static constexpr int RB = D * 2;           // bytes per LDS row
+  static constexpr int WAVE_LDS = 2 * 16 * RB;
+};
+
+// chunk position of (row r, chunk c) inside an LDS row
+template <int CPR>
+__device__ __forceinline__ int swz(int r, int c) {
+  return c ^ ((r % (CPR / 2)) * 2);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
-  constexpr int NT = D / 32;        // 16-byte pieces per lane per key row = QK k-steps
+  using C = SmallCfg<D>;
+  constexpr int CPR = C::CPR, LPR = C::LPR, NLD = C::NLD, PF = C::PF, RB = C::RB;
+  constexpr int NT = D / 32;        // QK k-steps
   constexpr int NDT = D / 16;       // 16-wide d tiles of O^T
-  constexpr int VP = D + 16;        // LDS pitch of a V row (elements)
-  constexpr int DQ = D / 4;         // d range per lane group
-  constexpr int V_ELEMS = 4 * 32 * VP;
-  constexpr int EPI_FLOATS = 4 * 16 * D + 2 * 64;
-  constexpr int SMEM_BYTES = (V_ELEMS * 2 > EPI_FLOATS * 4) ? V_ELEMS * 2 : EPI_FLOATS * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[SMEM_BYTES];
-  uint16_t* smem = reinterpret_cast<uint16_t*>(smem_raw);
+  constexpr int EPI_BYTES = (4 * 16 * D + 2 * 64) * 4;
+  constexpr int SMEM_BYTES = (4 * C::WAVE_LDS > EPI_BYTES) ? 4 * C::WAVE_LDS : EPI_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -175,102 +201,114 @@ __global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
   const int head = it.kvh * G + (r - tok * G);
   const int row_limit = a.causal ? tok + Lk - Lq : INT_MAX;
 
+  // Q^T operand: k-step t, slot j <-> d = 32t + 8g + j
   bf16x8_t qf[NT];
   if (row_ok) {
-    const uint16_t* qp = a.q + ((int64_t)(t0 + tok) * a.H + head) * D + g * DQ;
+    const uint16_t* qp = a.q + ((int64_t)(t0 + tok) * a.H + head) * D + 8 * g;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) qf[t] = ld16(qp + 8 * t);
+    for (int t = 0; t < NT; ++t) qf[t] = ld16(qp + 32 * t);
   } else {
 #pragma unroll
     for (int t = 0; t < NT; ++t) qf[t] = zero8();
   }
 
+  // loader geometry: this lane reads chunk lc of rows lr + LPR*i
+  const int lr = lane / CPR, lc = lane % CPR;
   const int64_t row_elems = (int64_t)a.Hkv * D;
-  const uint16_t* kbase = a.cache + (int64_t)it.kvh * D + g * DQ;
+  const uint16_t* kbase = a.cache + (int64_t)it.kvh * D + lc * 8;
   const int32_t* btrow = a.block_table + (int64_t)it.seq * a.bt_stride;
-  uint16_t* vl = smem + wave * 32 * VP;
+  uint8_t* wl = smem + wave * C::WAVE_LDS;       // K rows [0,16), V rows [16,32)
+
+  const int nsteps = (kv1 > kv0 + wave * 16) ? (kv1 - kv0 - wave * 16 + 63) / 64 : 0;
+
+  u32x4_t buf[PF][2 * NLD];
+  auto issue = [&](u32x4_t* bf, int st) {
+    const int kb = kv0 + 16 * (wave + 4 * st);
+    const int phys = btrow[kb / a.BS];
+    const uint16_t* p = kbase + ((int64_t)phys * a.BS + kb % a.BS + lr) * row_elems;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      if (kb + lr + LPR * i < kv1) {
+        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(p + (int64_t)LPR * i * row_elems);
+        bf[i] = __builtin_nontemporal_load(src);
+        bf[NLD + i] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(src) + a.plane));
+      } else {
+        bf[i] = u32x4_t{0u, 0u, 0u, 0u};
+        bf[NLD + i] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+  };
 
   float m_run = kNegInf, l_run = 0.f;
   f32x4_t o[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int kb = kv0 + wave * 32; kb < kv1; kb += 4 * 32) {
-    bf16x8_t k0[NT], k1[NT], v0[NT], v1[NT];
-    const int key0 = kb + n, key1 = kb + 16 + n;
-    if (key0 < kv1) {
-      const int phys = btrow[key0 / a.BS];
-      const uint16_t* p = kbase + ((int64_t)phys * a.BS + key0 % a.BS) * row_elems;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) { k0[t] = ld16(p + 8 * t); v0[t] = ld16(p + a.plane + 8 * t); }
-    } else {
+  for (int p = 0; p < PF; ++p)
+    if (p < nsteps) issue(buf[p], p);
+
+  // LDS addresses that do not change between steps
+  const int vr = 4 * g + (n >> 2);                         // V row of this lane's transposing read
+  for (int it0 = 0; it0 < nsteps; it0 += PF) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) { k0[t] = zero8(); v0[t] = zero8(); }
-    }
-    if (key1 < kv1) {
-      const int phys = btrow[key1 / a.BS];
-      const uint16_t* p = kbase + ((int64_t)phys * a.BS + key1 % a.BS) * row_elems;
+    for (int p = 0; p < PF; ++p) {
+      const int st = it0 + p;
+      if (st >= nsteps) break;
+      // stage step st (swizzled) in this wave's LDS tile
 #pragma unroll
-      for (int t = 0; t < NT; ++t) { k1[t] = ld16(p + 8 * t); v1[t] = ld16(p + a.plane + 8 * t); }
-    } else {
+      for (int i = 0; i < NLD; ++i) {
+        const int row = lr + LPR * i;
+        *reinterpret_cast<u32x4_t*>(wl + row * RB + swz<CPR>(row, lc) * 16) = buf[p][i];
+        *reinterpret_cast<u32x4_t*>(wl + (16 + row) * RB + swz<CPR>(row, lc) * 16) = buf[p][NLD + i];
+      }
+      if (st + PF < nsteps) issue(buf[p], st + PF);
+      const int kb = kv0 + 16 * (wave + 4 * st);
+
+      // S^T (16 keys x 16 rows): lane (n, g) reg i <- key kb + 4g + i
+      f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < NT; ++t) { k1[t] = zero8(); v1[t] = zero8(); }
-    }
-    // stage V rows [key][d] of this step in the wave's LDS tile
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8_t ka =
+            *reinterpret_cast<const bf16x8_t*>(wl + n * RB + swz<CPR>(n, 4 * t + g) * 16);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[t], s, 0, 0, 0);
+      }
+      float x[4];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      *reinterpret_cast<bf16x8_t*>(vl + n * VP + g * DQ + 8 * t) = v0[t];
-      *reinterpret_cast<bf16x8_t*>(vl + (16 + n) * VP + g * DQ + 8 * t) = v1[t];
-    }
-    // S^T tiles: lane (n, g) reg i <- score of key kb + 4g + i (s0) and
-    // kb + 16 + 4g + i (s1) for row n
-    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < 4; ++i) {
+        const int key = kb + 4 * g + i;
+        x[i] = (key >= kv1 || key > row_limit) ? kNegInf : s[i] * a.scale_log2;
+      }
+      float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      mx = wave_max_xor(mx, 16);
+      mx = wave_max_xor(mx, 32);
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      float pr[4];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0[t], qf[t], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[t], qf[t], s1, 0, 0, 0);
-    }
-    float x[8];
+      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
+      l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+      m_run = m_new;
+      // rescale O only when some row's running max moved
+      if (__any(alpha != 1.f)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = s0[i] * a.scale_log2;
-      x[4 + i] = s1[i] * a.scale_log2;
-    }
-    // tail and causal mask (cheap next to the loads, so always applied)
+        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+      }
+      uint2 pw;
+      pw.x = pack_bf16x2(pr[0], pr[1]);
+      pw.y = pack_bf16x2(pr[2], pr[3]);
+      const bf16x4_t pb = __builtin_bit_cast(bf16x4_t, pw);
+      // O^T += V^T P^T; lane (s, g) of each 16-lane group reads 4 d of key
+      // 4g + s/4, so lane s receives d = 16dt + s of keys 4g..4g+3
+      const uint8_t* vrow = wl + (16 + vr) * RB + 8 * (n & 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ka = kb + 4 * g + i, kc = kb + 16 + 4 * g + i;
-      if (ka >= kv1 || ka > row_limit) x[i] = kNegInf;
-      if (kc >= kv1 || kc > row_limit) x[4 + i] = kNegInf;
-    }
-    float mx = x[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-    mx = wave_max_xor(mx, 16);
-    mx = wave_max_xor(mx, 32);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float p[8], ps = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
-      ps += p[i];
-    }
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-    const bf16x8_t pb = pack_bf16x8(p);
-    // O^T += V^T P^T: A operand = 16 d x 32 keys read transposed from LDS;
-    // slots 0-3 hold keys 4g..4g+3, slots 4-7 keys 16+4g..16+4g+3, which is
-    // where the S^T layout left this lane's probabilities
-    const uint16_t* vr0 = vl + (4 * g + (n >> 2)) * VP + 4 * (n & 3);
-    const uint16_t* vr1 = vr0 + 16 * VP;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const bf16x8_t av = cat(lds_read_tr(vr0 + 16 * dt), lds_read_tr(vr1 + 16 * dt));
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, o[dt], 0, 0, 0);
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int chunk = 2 * dt + ((n & 3) >> 1);
+        const bf16x4_t av = lds_read_tr(reinterpret_cast<const uint16_t*>(vrow + swz<CPR>(vr, chunk) * 16));
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pb, o[dt], 0, 0, 0);
+      }
     }
   }
 
@@ -278,7 +316,7 @@ __global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
   __syncthreads();
-  float* so = reinterpret_cast<float*>(smem_raw);
+  float* so = reinterpret_cast<float*>(smem);
   float* sm = so + 4 * 16 * D;
   float* sl = sm + 64;
 #pragma unroll
@@ -309,10 +347,10 @@ __global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
     float acc[DPT];
 #pragma unroll
     for (int e = 0; e < DPT; ++e) {
-      float s = 0.f;
+      float sum = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) s += wt[w] * so[(w * 16 + er) * D + ec * DPT + e];
-      acc[e] = s * inv;
+      for (int w = 0; w < 4; ++w) sum += wt[w] * so[(w * 16 + er) * D + ec * DPT + e];
+      acc[e] = sum * inv;
     }
     const int rr = it.row0 + er;
     const int etok = rr / G;
@@ -531,7 +569,10 @@ __global__ __launch_bounds__(256) void attn_tiled_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-KV reduction: one workgroup per reduce item, one wave per row.
+// Split-KV reduction: one workgroup per (reduce item, row); its 4 waves take
+// every 4th split, each lane D/64 elements of the row, and the waves'
+// partial sums meet in LDS.  Partials hold O normalised by its own row sum
+// and the natural-log lse of that split.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void split_reduce_kernel(
@@ -540,49 +581,66 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(
     float* __restrict__ lse, int H, int G) {
   constexpr int EPL = D / 64;
   static_assert(EPL >= 1, "split reduce");
+  __shared__ float s_m[4], s_l[4];
+  __shared__ __attribute__((aligned(16))) float s_o[4][D];
   const int32_t* p = ritems + (int64_t)blockIdx.x * PA_ITEM_WORDS;
   const int seq = p[0], kvh = p[1], row0 = p[2], prow_n = p[3], prow0 = p[4], nsplit = p[5];
+  const int row = blockIdx.y;
   const int t0 = cu[seq];
   const int Lq = cu[seq + 1] - t0;
   const int nrows = min(prow_n, Lq * G - row0);
+  if (row >= nrows) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int row = wave; row < nrows; row += 4) {
-    float M = kNegInf;
-    for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, part_lse[prow0 + s * prow_n + row]);
+
+  float M = kNegInf;
+  for (int s = threadIdx.x; s < nsplit; s += 256) M = fmaxf(M, part_lse[prow0 + s * prow_n + row]);
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) M = wave_max_xor(M, m);
-    float acc[EPL];
+  for (int m = 32; m >= 1; m >>= 1) M = wave_max_xor(M, m);
+  if (lane == 0) s_m[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+
+  float acc[EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-    float L = 0.f;
-    if (M != kNegInf) {
-      for (int s = 0; s < nsplit; ++s) {
-        const int pr = prow0 + s * prow_n + row;
-        const float ls = part_lse[pr];
-        const float w = (ls == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((ls - M) * kLog2e);
-        L += w;
-        const float* src = part_o + (int64_t)pr * D + lane * EPL;
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  float L = 0.f;
+  if (M != kNegInf) {
+#pragma unroll 4
+    for (int s = wave; s < nsplit; s += 4) {
+      const int pr = prow0 + s * prow_n + row;
+      const float ls = part_lse[pr];
+      const float w = (ls == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((ls - M) * kLog2e);
+      L += w;
+      const float* src = part_o + (int64_t)pr * D + lane * EPL;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] += w * src[e];
-      }
+      for (int e = 0; e < EPL; ++e) acc[e] += w * src[e];
     }
-    const bool empty = !(L > 0.f);
-    const float inv = empty ? 0.f : 1.f / L;
-    const int rr = row0 + row;
-    const int tok = rr / G;
-    const int head = kvh * G + (rr - tok * G);
-    const int64_t orow = (int64_t)(t0 + tok) * H + head;
-    uint16_t* op = out + orow * D + lane * EPL;
-#pragma unroll
-    for (int e = 0; e < EPL; e += 2) {
-      if (EPL == 1) {
-        op[0] = (uint16_t)(pack_bf16x2(acc[0] * inv, 0.f) & 0xffffu);
-      } else {
-        *reinterpret_cast<uint32_t*>(op + e) = pack_bf16x2(acc[e] * inv, acc[e + 1] * inv);
-      }
-    }
-    if (lane == 0 && lse) lse[orow] = empty ? kNegInf : M + __logf(L);
   }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) s_o[wave][lane * EPL + e] = acc[e];
+  if (lane == 0) s_l[wave] = L;
+  __syncthreads();
+  if (wave != 0) return;
+  L = (s_l[0] + s_l[1]) + (s_l[2] + s_l[3]);
+  const bool empty = !(L > 0.f);
+  const float inv = empty ? 0.f : 1.f / L;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e)
+    acc[e] = ((s_o[0][lane * EPL + e] + s_o[1][lane * EPL + e]) +
+              (s_o[2][lane * EPL + e] + s_o[3][lane * EPL + e])) * inv;
+  const int rr = row0 + row;
+  const int tok = rr / G;
+  const int head = kvh * G + (rr - tok * G);
+  const int64_t orow = (int64_t)(t0 + tok) * H + head;
+  uint16_t* op = out + orow * D + lane * EPL;
+  if constexpr (EPL == 1) {
+    op[0] = (uint16_t)(pack_bf16x2(acc[0], 0.f) & 0xffffu);
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; e += 2)
+      *reinterpret_cast<uint32_t*>(op + e) = pack_bf16x2(acc[e], acc[e + 1]);
+  }
+  if (lane == 0 && lse) lse[orow] = empty ? kNegInf : M + __logf(L);
 }
 
 // ---------------------------------------------------------------------------
@@ -643,7 +701,8 @@ pa_status launch_fwd(const AttnArgs& base, const pa_plan_info* plan, const int32
   if (plan->num_reduce_items > 0) {
     const int32_t* r =
         items + (int64_t)(plan->num_small_items + plan->num_tiled_items) * PA_ITEM_WORDS;
-    hipLaunchKernelGGL(split_reduce_kernel<D>, dim3(plan->num_reduce_items), dim3(256), 0, stream,
+    hipLaunchKernelGGL(split_reduce_kernel<D>, dim3(plan->num_reduce_items, plan->max_reduce_rows),
+                       dim3(256), 0, stream,
                        r, base.part_o, base.part_lse, base.cu, base.out, base.lse, base.H, base.G);
   }
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
@@ -694,7 +753,8 @@ pa_status pa_varlen_fwd(const pa_attn_params* p, const pa_plan_info* plan, const
       plan->causal != p->causal || plan->num_tokens != num_tokens)
     return PA_ERR_INVALID_ARGUMENT;
   if (plan->num_small_items < 0 || plan->num_tiled_items < 0 || plan->num_reduce_items < 0 ||
-      plan->num_partial_rows < 0)
+      plan->num_partial_rows < 0 || plan->max_reduce_rows < 0 ||
+      plan->max_reduce_rows > PA_TILED_ROWS || (plan->num_reduce_items > 0 && plan->max_reduce_rows == 0))
     return PA_ERR_INVALID_ARGUMENT;
   const int64_t n_items =
       (int64_t)plan->num_small_items + plan->num_tiled_items + plan->num_reduce_items;

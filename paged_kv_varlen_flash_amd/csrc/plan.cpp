@@ -179,6 +179,8 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
   info->num_tiled_items = (int32_t)tiled_items.size();
   info->num_reduce_items = (int32_t)reduce_items.size();
   info->num_partial_rows = (int32_t)prow;
+  info->max_reduce_rows = 0;
+  for (const Item& it : reduce_items) info->max_reduce_rows = std::max(info->max_reduce_rows, it.w[3]);
   info->batch = B;
   info->num_heads = H;
   info->num_kv_heads = Hkv;

@@ -55,6 +55,7 @@ class AttnParams(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [("num_small_items", ctypes.c_int32), ("num_tiled_items", ctypes.c_int32),
                 ("num_reduce_items", ctypes.c_int32), ("num_partial_rows", ctypes.c_int32),
+                ("max_reduce_rows", ctypes.c_int32),
                 ("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_size", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
