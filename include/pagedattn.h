@@ -66,7 +66,7 @@ extern const int32_t pa_supported_head_sizes[PA_NUM_HEAD_SIZES]; /* {64, 128, 25
  *                      max_blocks_per_seq (a column slice such as the cascade
  *                      suffix view block_table[:, k:] keeps the full stride)
  *   causal             0 or 1
- *   scale              softmax scale applied to q.k (fp32)            */
+ *   scale              softmax scale applied to q.k (fp32, finite, > 0) */
 typedef struct {
   int32_t batch;
   int32_t num_heads;

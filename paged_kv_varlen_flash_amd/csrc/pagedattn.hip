@@ -112,6 +112,7 @@ struct AttnArgs {
   float* part_lse;
   int64_t plane;      // elements in one cache plane (NB*BS*Hkv*D)
   int H, Hkv, G, BS, MB, bt_stride, causal;
+  int bs_log2;        // log2(BS) when BS is a power of two, else -1
   float scale_log2;   // scale * log2(e)
 };
 
@@ -383,17 +384,34 @@ __global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
 // Tiled attention: one workgroup of 4 waves per 128-row block; wave w owns
 // rows 32w..32w+31 (lane (n = lane%32, h = lane/32) owns row n and the key
 // half h of each 32x32 MFMA tile).  Key tiles of 64 keys are gathered
-// through the block table by all 256 threads into registers one tile ahead,
-// then stored to LDS (K with pitch D+8, V with pitch D+16 elements).
+// through the block table by all 256 threads into registers one tile ahead
+// (16 consecutive lanes per 256-byte key row), then stored to LDS: K with a
+// pitch of D+8 elements (conflict-free 16-byte operand reads), V with D+32
+// (the transposing reads of two 16-lane groups cover all banks once).
+//
+// Online softmax with a lazy rescale: a row keeps its reference max until
+// the tile max exceeds it by more than kRescaleSlack (log2 units), so the
+// O accumulators are rescaled only when some row of the wave jumps.  The
+// probabilities then stay below 2^kRescaleSlack, which bf16 and fp32
+// represent with the same relative precision; the final normalisation uses
+// the same reference, so the result is exact up to rounding.
 // ---------------------------------------------------------------------------
+constexpr float kRescaleSlack = 8.f;
+
+template <bool B>
+struct Bool {
+  static constexpr bool value = B;
+};
+
 template <int D>
-__global__ __launch_bounds__(256) void attn_tiled_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_tiled_kernel(AttnArgs a) {
   constexpr int NKT = D / 16;       // QK k-steps (16 d each)
   constexpr int NDT = D / 32;       // 32-wide d tiles of O^T
   constexpr int KP = D + 8;
-  constexpr int VP = D + 16;
+  constexpr int VP = D + 32;
   constexpr int CPR = D / 8;        // 16-byte chunks per key row
   constexpr int LOADS = 64 * CPR / 256;
+  constexpr int KSTEP = 256 / CPR;  // key rows covered by one pass of 256 threads
   static_assert(LOADS >= 1, "tile loader");
   __shared__ __attribute__((aligned(16))) uint16_t kl[64 * KP];
   __shared__ __attribute__((aligned(16))) uint16_t vl[64 * VP];
@@ -428,20 +446,35 @@ __global__ __launch_bounds__(256) void attn_tiled_kernel(AttnArgs a) {
     for (int t = 0; t < NKT; ++t) qf[t] = zero8();
   }
 
+  // loader: this thread moves chunk lcol of key rows lkey + KSTEP*i
+  const int lkey = tid / CPR, lcol = tid % CPR;
   const int64_t row_elems = (int64_t)a.Hkv * D;
-  const uint16_t* cbase = a.cache + (int64_t)it.kvh * D;
+  const uint16_t* cbase = a.cache + (int64_t)it.kvh * D + lcol * 8;
   const int32_t* btrow = a.block_table + (int64_t)it.seq * a.bt_stride;
+  const int bs_log2 = a.bs_log2;
 
   bf16x8_t kr[LOADS], vr[LOADS];
   auto load_tile = [&](int j0) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + 256 * i;
-      const int key = j0 + c / CPR;
-      const int col = c % CPR;
+      const int key = j0 + lkey + KSTEP * i;
       if (key < kv1) {
-        const int phys = btrow[key / a.BS];
-        const uint16_t* p = cbase + ((int64_t)phys * a.BS + key % a.BS) * row_elems + col * 8;
+        int blk, off;
+        if constexpr (KSTEP <= 16) {
+          // tiles start on a multiple of 16 and blocks hold a multiple of 16
+          // keys, so the KSTEP keys of pass i share one block: a scalar lookup
+          const int kg = j0 + KSTEP * i;
+          blk = (bs_log2 >= 0) ? (kg >> bs_log2) : (kg / a.BS);
+          off = kg - blk * a.BS + lkey;
+        } else if (bs_log2 >= 0) {
+          blk = key >> bs_log2;
+          off = key & (a.BS - 1);
+        } else {
+          blk = key / a.BS;
+          off = key - blk * a.BS;
+        }
+        const int phys = btrow[blk];
+        const uint16_t* p = cbase + (int64_t)phys * a.BS * row_elems + (int64_t)off * row_elems;
         kr[i] = ld16(p);
         vr[i] = ld16(p + a.plane);
       } else {
@@ -458,65 +491,59 @@ __global__ __launch_bounds__(256) void attn_tiled_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
 
-  int j0 = it.kv0;
-  if (j0 < kv1) load_tile(j0);
   const int q16 = lane >> 4, s16 = lane & 15;
-  for (; j0 < kv1; j0 += 64) {
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + 256 * i;
-      const int key = c / CPR, col = c % CPR;
-      *reinterpret_cast<bf16x8_t*>(kl + key * KP + col * 8) = kr[i];
-      *reinterpret_cast<bf16x8_t*>(vl + key * VP + col * 8) = vr[i];
-    }
-    __syncthreads();
-    if (j0 + 64 < kv1) load_tile(j0 + 64);
+  const uint16_t* kp0 = kl + n * KP + 8 * h;
+  const uint16_t* vp0 = vl + (4 * h + (s16 >> 2)) * VP + 16 * (q16 & 1) + 4 * (s16 & 3);
 
+  auto tile = [&](int j0, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     // S^T: two 32-key tiles; lane (n, h) reg i <- key j0 + 32u + 8(i/4) + 4h + i%4
     f32x16_t s[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[u][i] = 0.f;
-      const uint16_t* kp = kl + (32 * u + n) * KP + 8 * h;
 #pragma unroll
-      for (int t = 0; t < NKT; ++t) {
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kp + 16 * t);
+    for (int t = 0; t < NKT; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kp0 + 32 * u * KP + 16 * t);
         s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[t], s[u], 0, 0, 0);
       }
-    }
+    // raw scores; the scale (> 0) is applied inside the exponent, so the max
+    // is taken on raw scores and scaled once
     float x[32];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) x[16 * u + i] = s[u][i] * a.scale_log2;
-    if (j0 + 64 > kv1 || j0 + 63 > wave_limit) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < 16; ++i) {
+        float v = s[u][i];
+        if constexpr (MASKED) {
           const int key = j0 + 32 * u + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (key >= kv1 || key > row_limit) x[16 * u + i] = kNegInf;
+          v = (key >= kv1 || key > row_limit) ? kNegInf : v;
         }
-    }
+        x[16 * u + i] = v;
+      }
     float mx = x[0];
 #pragma unroll
     for (int i = 1; i < 32; ++i) mx = fmaxf(mx, x[i]);
-    mx = wave_max_xor(mx, 32);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    mx = wave_max_xor(mx, 32) * a.scale_log2;
+    if (__builtin_expect(__any(mx > m_run + kRescaleSlack), 0)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
     float ps = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      x[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
+      x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], a.scale_log2, neg_m));
       ps += x[i];
     }
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+    l_run += ps;
     // P^T operands for the four 16-key steps: step ks = 2u + half uses
     // regs 8*half .. 8*half+7 of tile u
     bf16x8_t pb[4];
@@ -526,14 +553,31 @@ __global__ __launch_bounds__(256) void attn_tiled_kernel(AttnArgs a) {
     // kb+8+4h+0..3 with kb = 16*ks, read transposed from LDS per 16-lane group
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const uint16_t* vr0 = vl + (16 * ks + 4 * h + (s16 >> 2)) * VP + 16 * (q16 & 1) + 4 * (s16 & 3);
-      const uint16_t* vr1 = vr0 + 8 * VP;
+      const uint16_t* vr0 = vp0 + 16 * ks * VP;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const bf16x8_t av = cat(lds_read_tr(vr0 + 32 * dt), lds_read_tr(vr1 + 32 * dt));
+        const bf16x8_t av = cat(lds_read_tr(vr0 + 32 * dt), lds_read_tr(vr0 + 8 * VP + 32 * dt));
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks], o[dt], 0, 0, 0);
       }
     }
+  };
+
+  int j0 = it.kv0;
+  if (j0 < kv1) load_tile(j0);
+  for (; j0 < kv1; j0 += 64) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int key = lkey + KSTEP * i;
+      *reinterpret_cast<bf16x8_t*>(kl + key * KP + lcol * 8) = kr[i];
+      *reinterpret_cast<bf16x8_t*>(vl + key * VP + lcol * 8) = vr[i];
+    }
+    __syncthreads();
+    if (j0 + 64 < kv1) load_tile(j0 + 64);
+    if (j0 + 64 > kv1 || j0 + 63 > wave_limit)
+      tile(j0, Bool<true>{});
+    else
+      tile(j0, Bool<false>{});
   }
 
   l_run += __shfl_xor(l_run, 32);
@@ -793,6 +837,9 @@ pa_status pa_varlen_fwd(const pa_attn_params* p, const pa_plan_info* plan, const
   a.MB = p->max_blocks_per_seq;
   a.bt_stride = p->block_table_stride ? p->block_table_stride : p->max_blocks_per_seq;
   a.causal = p->causal;
+  a.bs_log2 = -1;
+  for (int b = 0; b < 31; ++b)
+    if ((1 << b) == p->block_size) a.bs_log2 = b;
   a.scale_log2 = p->scale * kLog2e;
   switch (p->head_size) {
     case 64: return launch_fwd<64>(a, plan, worklist, stream);

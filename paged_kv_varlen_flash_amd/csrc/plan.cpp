@@ -39,7 +39,8 @@ pa_status check_params(const pa_attn_params* p) {
     return PA_ERR_INVALID_ARGUMENT;
   if ((int64_t)p->max_blocks_per_seq * p->block_size > INT32_MAX / 2) return PA_ERR_INVALID_ARGUMENT;
   if (p->causal != 0 && p->causal != 1) return PA_ERR_INVALID_ARGUMENT;
-  if (!std::isfinite(p->scale)) return PA_ERR_INVALID_ARGUMENT;
+  // a softmax scale is positive (the kernels take row maxima on unscaled scores)
+  if (!std::isfinite(p->scale) || !(p->scale > 0.f)) return PA_ERR_INVALID_ARGUMENT;
   // byte offsets into the cache must fit in 64 bits with room to spare, and
   // every per-launch index the kernels form in 32 bits must fit
   const int64_t plane = (int64_t)p->num_blocks * p->block_size * p->num_kv_heads * p->head_size;
