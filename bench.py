@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+CALIB_BYTES = 256 << 20        # size of the counter-calibration copy
 BF16_PEAK_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense
 
 
@@ -159,6 +160,30 @@ def time_attention(step, reps, flush):
     return float(times.mean()), float(np.median(times))
 
 
+def source_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("pagedattn.hip", "plan.cpp", "plan_internal.h"):
+        with open(os.path.join(ROOT, "paged_kv_varlen_flash_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload):
+    """HBM bytes per launch of the attention call from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE passes (profiles/traffic.json), or None
+    when the kernel sources changed since those counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != source_sha256():
+        return None
+    return rec
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -222,6 +247,13 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # one plain 256 MiB device copy (untimed): under rocprofv3 --pmc its
+    # FETCH_SIZE / WRITE_SIZE calibrate the counters against known bytes
+    calib_src = torch.ones(CALIB_BYTES, dtype=torch.uint8, device=dev)
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
 
     head = measure(args.workload, args, dev, flush, not args.no_cpu_baseline)
     wl = head["wl"]
@@ -229,8 +261,12 @@ def main():
     value = head["kv_bytes"] / (head["ms_per_step"] * 1e-3) / 1e9
     if decode_like:
         ach = head["kv_bytes"] / head["attn_mean_s"] / 1e9
+        tr = recorded_traffic(args.workload)
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": (tr["read_bytes"] + tr["write_bytes"]) if tr else None,
+                "traffic_read_over_algorithmic": (round(tr["read_bytes"] / head["kv_bytes"], 4)
+                                                  if tr else None),
                 "kernel": "pa_varlen_fwd (attn_small_kernel<%d> + split_reduce_kernel<%d>)"
                           % (wl.D, wl.D),
                 "per_launch_bytes": head["kv_bytes"],
