@@ -83,19 +83,28 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask));
 }
 
+// Load of a wave-uniform int32 from memory that no kernel of the launch
+// writes (work list, lengths, block table): through the constant address
+// space, so it becomes a scalar load instead of a vector load whose wait
+// would also wait for every prefetch in flight.
+__device__ __forceinline__ int32_t ld_uniform(const int32_t* p) {
+  typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+  return *(const_i32_ptr)(reinterpret_cast<uintptr_t>(p));
+}
+
 struct Item {
   int seq, kvh, row0, nrows, kv0, kv1, prow;
 };
 
 __device__ __forceinline__ Item load_item(const int32_t* p) {
   Item it;
-  it.seq = p[0];
-  it.kvh = p[1];
-  it.row0 = p[2];
-  it.nrows = p[3];
-  it.kv0 = p[4];
-  it.kv1 = p[5];
-  it.prow = p[6];
+  it.seq = ld_uniform(p + 0);
+  it.kvh = ld_uniform(p + 1);
+  it.row0 = ld_uniform(p + 2);
+  it.nrows = ld_uniform(p + 3);
+  it.kv0 = ld_uniform(p + 4);
+  it.kv1 = ld_uniform(p + 5);
+  it.prow = ld_uniform(p + 6);
   return it;
 }
 
@@ -185,12 +194,13 @@ __global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM_BYTES];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int n = lane & 15, g = lane >> 4;
   const Item it = load_item(a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS);
-  const int t0 = a.cu[it.seq];
-  const int Lq = a.cu[it.seq + 1] - t0;
-  const int Lk = a.seqused_k[it.seq];
+  const int t0 = ld_uniform(a.cu + it.seq);
+  const int Lq = ld_uniform(a.cu + it.seq + 1) - t0;
+  const int Lk = ld_uniform(a.seqused_k + it.seq);
   const int G = a.G;
   const int nrows = min(it.nrows, Lq * G - it.row0);
   const int kv1 = min(min(it.kv1, Lk), a.MB * a.BS);
@@ -225,7 +235,7 @@ __global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
   u32x4_t buf[PF][2 * NLD];
   auto issue = [&](u32x4_t* bf, int st) {
     const int kb = kv0 + 16 * (wave + 4 * st);
-    const int phys = btrow[kb / a.BS];
+    const int phys = ld_uniform(btrow + kb / a.BS);
     const uint16_t* p = kbase + ((int64_t)phys * a.BS + kb % a.BS + lr) * row_elems;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
@@ -413,16 +423,18 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_tiled_kernel(Att
   constexpr int LOADS = 64 * CPR / 256;
   constexpr int KSTEP = 256 / CPR;  // key rows covered by one pass of 256 threads
   static_assert(LOADS >= 1, "tile loader");
-  __shared__ __attribute__((aligned(16))) uint16_t kl[64 * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t vl[64 * VP];
+  // two K/V tile buffers: tile j is computed from buffer j%2 while tile j+1's
+  // registers land in the other one
+  __shared__ __attribute__((aligned(16))) uint16_t kl[2][64 * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t vl[2][64 * VP];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
   const Item it = load_item(a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS);
-  const int t0 = a.cu[it.seq];
-  const int Lq = a.cu[it.seq + 1] - t0;
-  const int Lk = a.seqused_k[it.seq];
+  const int t0 = ld_uniform(a.cu + it.seq);
+  const int Lq = ld_uniform(a.cu + it.seq + 1) - t0;
+  const int Lk = ld_uniform(a.seqused_k + it.seq);
   const int G = a.G;
   const int nrows = min(it.nrows, Lq * G - it.row0);
   const int kv1 = min(min(it.kv1, Lk), a.MB * a.BS);
@@ -445,6 +457,10 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_tiled_kernel(Att
 #pragma unroll
     for (int t = 0; t < NKT; ++t) qf[t] = zero8();
   }
+  // Q must have landed before the loop: otherwise the wait-count pass treats
+  // the Q loads as possibly in flight inside the loop and makes every QK
+  // MFMA wait for the next tile's prefetch loads as well
+  __builtin_amdgcn_s_waitcnt(0);
 
   // loader: this thread moves chunk lcol of key rows lkey + KSTEP*i
   const int lkey = tid / CPR, lcol = tid % CPR;
@@ -455,31 +471,50 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_tiled_kernel(Att
 
   bf16x8_t kr[LOADS], vr[LOADS];
   auto load_tile = [&](int j0) {
+    if constexpr (KSTEP <= 16) {
+      // tiles start on a multiple of 16 and blocks hold a multiple of 16
+      // keys, so the KSTEP keys of pass i share one block: the lookups are
+      // wave-uniform, done as scalar loads outside the per-lane tail branch
+      int phys[LOADS], base[LOADS];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int key = j0 + lkey + KSTEP * i;
-      if (key < kv1) {
-        int blk, off;
-        if constexpr (KSTEP <= 16) {
-          // tiles start on a multiple of 16 and blocks hold a multiple of 16
-          // keys, so the KSTEP keys of pass i share one block: a scalar lookup
-          const int kg = j0 + KSTEP * i;
-          blk = (bs_log2 >= 0) ? (kg >> bs_log2) : (kg / a.BS);
-          off = kg - blk * a.BS + lkey;
-        } else if (bs_log2 >= 0) {
-          blk = key >> bs_log2;
-          off = key & (a.BS - 1);
+      for (int i = 0; i < LOADS; ++i) {
+        const int kg = min(j0 + KSTEP * i, kv1 - 1);
+        const int blk = (bs_log2 >= 0) ? (kg >> bs_log2) : (kg / a.BS);
+        base[i] = (j0 + KSTEP * i) - blk * a.BS;
+        phys[i] = ld_uniform(btrow + blk);
+      }
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int key = j0 + lkey + KSTEP * i;
+        if (key < kv1) {
+          const uint16_t* p = cbase + ((int64_t)phys[i] * a.BS + base[i] + lkey) * row_elems;
+          kr[i] = ld16(p);
+          vr[i] = ld16(p + a.plane);
         } else {
-          blk = key / a.BS;
-          off = key - blk * a.BS;
+          kr[i] = zero8();
+          vr[i] = zero8();
         }
-        const int phys = btrow[blk];
-        const uint16_t* p = cbase + (int64_t)phys * a.BS * row_elems + (int64_t)off * row_elems;
-        kr[i] = ld16(p);
-        vr[i] = ld16(p + a.plane);
-      } else {
-        kr[i] = zero8();
-        vr[i] = zero8();
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int key = j0 + lkey + KSTEP * i;
+        if (key < kv1) {
+          int blk, off;
+          if (bs_log2 >= 0) {
+            blk = key >> bs_log2;
+            off = key & (a.BS - 1);
+          } else {
+            blk = key / a.BS;
+            off = key - blk * a.BS;
+          }
+          const uint16_t* p = cbase + ((int64_t)btrow[blk] * a.BS + off) * row_elems;
+          kr[i] = ld16(p);
+          vr[i] = ld16(p + a.plane);
+        } else {
+          kr[i] = zero8();
+          vr[i] = zero8();
+        }
       }
     }
   };
@@ -492,11 +527,13 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_tiled_kernel(Att
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
 
   const int q16 = lane >> 4, s16 = lane & 15;
-  const uint16_t* kp0 = kl + n * KP + 8 * h;
-  const uint16_t* vp0 = vl + (4 * h + (s16 >> 2)) * VP + 16 * (q16 & 1) + 4 * (s16 & 3);
+  const int koff = n * KP + 8 * h;
+  const int voff = (4 * h + (s16 >> 2)) * VP + 16 * (q16 & 1) + 4 * (s16 & 3);
 
-  auto tile = [&](int j0, auto masked) {
+  auto tile = [&](int j0, int buf, auto masked) {
     constexpr bool MASKED = decltype(masked)::value;
+    const uint16_t* kp0 = kl[buf] + koff;
+    const uint16_t* vp0 = vl[buf] + voff;
     // S^T: two 32-key tiles; lane (n, h) reg i <- key j0 + 32u + 8(i/4) + 4h + i%4
     f32x16_t s[2];
 #pragma unroll
@@ -562,22 +599,33 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_tiled_kernel(Att
     }
   };
 
-  int j0 = it.kv0;
-  if (j0 < kv1) load_tile(j0);
-  for (; j0 < kv1; j0 += 64) {
-    __syncthreads();
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int key = lkey + KSTEP * i;
-      *reinterpret_cast<bf16x8_t*>(kl + key * KP + lcol * 8) = kr[i];
-      *reinterpret_cast<bf16x8_t*>(vl + key * VP + lcol * 8) = vr[i];
+      *reinterpret_cast<bf16x8_t*>(kl[buf] + key * KP + lcol * 8) = kr[i];
+      *reinterpret_cast<bf16x8_t*>(vl[buf] + key * VP + lcol * 8) = vr[i];
     }
-    __syncthreads();
-    if (j0 + 64 < kv1) load_tile(j0 + 64);
+  };
+
+  // one barrier per tile: after it, buffer buf holds tile j0 and every wave
+  // has finished reading buffer buf^1 (tile j0-64), which the registers of
+  // tile j0+64 overwrite once this tile's compute is done
+  int j0 = it.kv0, buf = 0;
+  if (j0 < kv1) {
+    load_tile(j0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (; j0 < kv1; j0 += 64, buf ^= 1) {
+    const bool more = j0 + 64 < kv1;
+    if (more) load_tile(j0 + 64);
     if (j0 + 64 > kv1 || j0 + 63 > wave_limit)
-      tile(j0, Bool<true>{});
+      tile(j0, buf, Bool<true>{});
     else
-      tile(j0, Bool<false>{});
+      tile(j0, buf, Bool<false>{});
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
   }
 
   l_run += __shfl_xor(l_run, 32);
@@ -628,10 +676,11 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(
   __shared__ float s_m[4], s_l[4];
   __shared__ __attribute__((aligned(16))) float s_o[4][D];
   const int32_t* p = ritems + (int64_t)blockIdx.x * PA_ITEM_WORDS;
-  const int seq = p[0], kvh = p[1], row0 = p[2], prow_n = p[3], prow0 = p[4], nsplit = p[5];
+  const int seq = ld_uniform(p), kvh = ld_uniform(p + 1), row0 = ld_uniform(p + 2);
+  const int prow_n = ld_uniform(p + 3), prow0 = ld_uniform(p + 4), nsplit = ld_uniform(p + 5);
   const int row = blockIdx.y;
-  const int t0 = cu[seq];
-  const int Lq = cu[seq + 1] - t0;
+  const int t0 = ld_uniform(cu + seq);
+  const int Lq = ld_uniform(cu + seq + 1) - t0;
   const int nrows = min(prow_n, Lq * G - row0);
   if (row >= nrows) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
