@@ -457,10 +457,6 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_tiled_kernel(Att
 #pragma unroll
     for (int t = 0; t < NKT; ++t) qf[t] = zero8();
   }
-  // Q must have landed before the loop: otherwise the wait-count pass treats
-  // the Q loads as possibly in flight inside the loop and makes every QK
-  // MFMA wait for the next tile's prefetch loads as well
-  __builtin_amdgcn_s_waitcnt(0);
 
   // loader: this thread moves chunk lcol of key rows lkey + KSTEP*i
   const int lkey = tid / CPR, lcol = tid % CPR;
@@ -612,10 +608,13 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_tiled_kernel(Att
   // has finished reading buffer buf^1 (tile j0-64), which the registers of
   // tile j0+64 overwrite once this tile's compute is done
   int j0 = it.kv0, buf = 0;
-  if (j0 < kv1) {
-    load_tile(j0);
-    store_tile(0);
-  }
+  if (j0 < kv1) load_tile(j0);
+  // the first tile's loads and the Q loads are in flight together; all of
+  // them must have landed before the loop: otherwise the wait-count pass
+  // treats the Q loads as possibly in flight inside the loop and makes
+  // every QK MFMA wait for the next tile's prefetch loads as well
+  __builtin_amdgcn_s_waitcnt(0);
+  if (j0 < kv1) store_tile(0);
   __syncthreads();
   for (; j0 < kv1; j0 += 64, buf ^= 1) {
     const bool more = j0 + 64 < kv1;
