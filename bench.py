@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 CALIB_BYTES = 256 << 20        # size of the counter-calibration copy
 BF16_PEAK_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense
+PLAN_RING = 8                  # pinned work-list buffers in flight
 
 
 def parse():
@@ -63,10 +64,13 @@ class Step:
         self.sk = np.ascontiguousarray(wl.k_lens, np.int32)
         words, info = ops.pa_plan_varlen(self.params, self.cu, self.sk)
         self.cap = words.nbytes
-        # two pinned host buffers: the plan of step t is written while the copy
-        # of step t-1 may still be queued
-        self.pinned = [torch.empty(words.size, dtype=torch.int32).pin_memory() for _ in range(2)]
-        self.copy_done = [None, None]
+        # a ring of pinned host buffers: the plan of step t is written while the
+        # copies of earlier steps may still be queued; the host blocks only when
+        # it is PLAN_RING steps ahead of the GPU, so a late wake-up of the host
+        # thread does not drain the GPU queue
+        self.pinned = [torch.empty(words.size, dtype=torch.int32).pin_memory()
+                       for _ in range(PLAN_RING)]
+        self.copy_done = [None] * PLAN_RING
         self.worklist = torch.from_numpy(words).to(dev)
         self.info = info
         self.workspace = torch.empty(max(info.workspace_bytes, 256), dtype=torch.uint8, device=dev)
@@ -84,7 +88,7 @@ class Step:
     def plan(self):
         import torch
         ops = self.ops
-        k = self.i & 1
+        k = self.i % PLAN_RING
         self.i += 1
         if self.copy_done[k] is not None:
             self.copy_done[k].synchronize()

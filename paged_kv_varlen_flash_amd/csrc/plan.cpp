@@ -56,6 +56,41 @@ struct Unit {        // one (sequence, kv head, row block) with its visible key 
 };
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int32_t ceil_div32(int32_t a, int32_t b) { return (int32_t)(((uint32_t)a + (uint32_t)b - 1u) / (uint32_t)b); }
+
+struct Item {        // one work item and its cost (keys x rows)
+  int32_t w[PA_ITEM_WORDS];
+  int64_t cost;
+};
+
+// Writes items in order of decreasing cost, ties in list order, and returns
+// the end of what it wrote.  Costs are below 2^40 (keys < 2^30, rows <= 128)
+// so a cost and a list index pack into one 64-bit sort key.
+int32_t* emit_by_cost(const std::vector<Item>& items, int32_t* dst) {
+  const size_t n = items.size();
+  constexpr int kIdxBits = 24;
+  if (n < ((size_t)1 << kIdxBits)) {
+    thread_local std::vector<uint64_t> keys;
+    keys.resize(n);
+    for (size_t i = 0; i < n; ++i)
+      keys[i] = ((uint64_t)(((int64_t)1 << 40) - 1 - items[i].cost) << kIdxBits) | i;
+    std::sort(keys.begin(), keys.end());
+    for (size_t i = 0; i < n; ++i) {
+      std::memcpy(dst, items[keys[i] & (((uint64_t)1 << kIdxBits) - 1)].w, sizeof(Item::w));
+      dst += PA_ITEM_WORDS;
+    }
+    return dst;
+  }
+  std::vector<size_t> order(n);
+  for (size_t i = 0; i < n; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](size_t a, size_t b) { return items[a].cost > items[b].cost; });
+  for (size_t i : order) {
+    std::memcpy(dst, items[i].w, sizeof(Item::w));
+    dst += PA_ITEM_WORDS;
+  }
+  return dst;
+}
 
 }  // namespace
 
@@ -79,8 +114,11 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
   const int32_t T = B > 0 ? cu[B] : 0;
   if ((int64_t)T * H > INT32_MAX) return PA_ERR_INVALID_ARGUMENT;
 
-  // ---- units: (seq, kvh, row block) with their visible key range
-  std::vector<Unit> units;
+  // ---- units: (seq, kvh, row block) with their visible key range.  The
+  // vectors are per thread and keep their capacity between calls: the planner
+  // runs once per step on the host, and allocation would dominate its cost.
+  thread_local std::vector<Unit> units;
+  units.clear();
   for (int32_t b = 0; b < B; ++b) {
     const int32_t Lq = cu[b + 1] - cu[b], Lk = sk[b];
     if (Lq == 0) continue;
@@ -127,27 +165,32 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
     }
   }
 
-  struct Item { int32_t w[PA_ITEM_WORDS]; int64_t cost; };
-  std::vector<Item> small_items, tiled_items, reduce_items;
+  thread_local std::vector<Item> small_items, tiled_items, reduce_items;
+  small_items.clear();
+  tiled_items.clear();
+  reduce_items.clear();
   int64_t prow = 0;
   for (const Unit& u : units) {
     // planner-chosen cuts fall on whole steps of the kernel; forced splits
     // (tests) only keep ranges a multiple of 16 keys so tiny inputs still split
-    const int64_t align = force_splits > 0 ? 16 : (u.small ? kSmallChunkAlign : kKeyTile);
-    int64_t nsplit = 1, chunk = u.kv_end;
-    if (u.kv_end > 0) {
+    // (32-bit arithmetic: key counts are below 2^30, and 64-bit divisions
+    // would dominate the planner's time)
+    const int32_t align = force_splits > 0 ? 16 : (u.small ? kSmallChunkAlign : kKeyTile);
+    const int32_t kv = u.kv_end;
+    int32_t nsplit = 1, chunk = kv;
+    if (kv > 0) {
       if (force_splits > 0) {
-        chunk = ceil_div(ceil_div(u.kv_end, force_splits), align) * align;
+        chunk = ceil_div32(ceil_div32(kv, force_splits), align) * align;
       } else {
         const int64_t c = u.small ? small_chunk : tiled_chunk;
-        if (c > 0 && u.kv_end > c) {
+        if (c > 0 && kv > c) {
           // equal-sized pieces, each a multiple of the alignment
-          const int64_t n = ceil_div(u.kv_end, c);
-          chunk = ceil_div(ceil_div(u.kv_end, n), align) * align;
+          const int32_t n = ceil_div32(kv, (int32_t)c);
+          chunk = ceil_div32(ceil_div32(kv, n), align) * align;
         }
       }
-      chunk = std::max<int64_t>(chunk, align);
-      nsplit = ceil_div(u.kv_end, chunk);
+      chunk = std::max(chunk, align);
+      nsplit = ceil_div32(kv, chunk);
     }
     auto& dst = u.small ? small_items : tiled_items;
     if (nsplit <= 1) {
@@ -167,13 +210,6 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
     if (prow > INT32_MAX / 2) return PA_ERR_INVALID_ARGUMENT;
     reduce_items.push_back(Item{{u.seq, u.kvh, u.row0, u.nrows, (int32_t)base, (int32_t)nsplit, 0, 0}, 0});
   }
-  // longest work first, so the tail of the launch is short items (stable:
-  // equal costs keep the (seq, kv head) order, which keeps a sequence's
-  // blocks close in time and their keys warm in L2)
-  auto by_cost = [](const Item& a, const Item& b) { return a.cost > b.cost; };
-  std::stable_sort(tiled_items.begin(), tiled_items.end(), by_cost);
-  std::stable_sort(small_items.begin(), small_items.end(), by_cost);
-
   const size_t n_items = small_items.size() + tiled_items.size() + reduce_items.size();
   const size_t words = PA_WORKLIST_HEADER_WORDS + n_items * PA_ITEM_WORDS;
   info->num_small_items = (int32_t)small_items.size();
@@ -204,12 +240,16 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
   wl[5] = info->num_partial_rows;
   wl[6] = G;
   wl[7] = p->causal;
+  // longest work first, so the tail of the launch is short items; equal
+  // costs keep the (seq, kv head) order, which keeps a sequence's blocks
+  // close in time and their keys warm in L2
   int32_t* dst = wl + PA_WORKLIST_HEADER_WORDS;
-  for (auto* v : {&small_items, &tiled_items, &reduce_items})
-    for (const Item& it : *v) {
-      std::memcpy(dst, it.w, sizeof(it.w));
-      dst += PA_ITEM_WORDS;
-    }
+  dst = emit_by_cost(small_items, dst);
+  dst = emit_by_cost(tiled_items, dst);
+  for (const Item& it : reduce_items) {
+    std::memcpy(dst, it.w, sizeof(it.w));
+    dst += PA_ITEM_WORDS;
+  }
   return PA_OK;
 }
 
