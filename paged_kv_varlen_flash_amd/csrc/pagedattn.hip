@@ -226,28 +226,40 @@ __global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
   // loader geometry: this lane reads chunk lc of rows lr + LPR*i
   const int lr = lane / CPR, lc = lane % CPR;
   const int64_t row_elems = (int64_t)a.Hkv * D;
-  const uint16_t* kbase = a.cache + (int64_t)it.kvh * D + lc * 8;
   const int32_t* btrow = a.block_table + (int64_t)it.seq * a.bt_stride;
   uint8_t* wl = smem + wave * C::WAVE_LDS;       // K rows [0,16), V rows [16,32)
 
   const int nsteps = (kv1 > kv0 + wave * 16) ? (kv1 - kv0 - wave * 16 + 63) / 64 : 0;
 
   u32x4_t buf[PF][2 * NLD];
+  // buffer loads: a step's rows past the key range (and steps past the
+  // range) read as zero without touching memory, so every step issues the
+  // same loads and the wait before each step counts exactly the later steps'
+  // loads still in flight
+  const int64_t kv_bytes = (int64_t)it.kvh * D * 2;
+  int voff[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) voff[i] = (lr + LPR * i) * (int)(row_elems * 2) + lc * 16;
+  const uint8_t* cache_b = reinterpret_cast<const uint8_t*>(a.cache);
   auto issue = [&](u32x4_t* bf, int st) {
     const int kb = kv0 + 16 * (wave + 4 * st);
-    const int phys = ld_uniform(btrow + kb / a.BS);
-    const uint16_t* p = kbase + ((int64_t)phys * a.BS + kb % a.BS + lr) * row_elems;
+    int nrec = 0;
+    int64_t boff = 0;
+    if (kb < kv1) {
+      const int blk = (a.bs_log2 >= 0) ? (kb >> a.bs_log2) : (kb / a.BS);
+      const int phys = ld_uniform(btrow + blk);
+      const int valid = min(16, kv1 - kb);
+      boff = ((int64_t)phys * a.BS + (kb - blk * a.BS)) * row_elems * 2 + kv_bytes;
+      nrec = (valid - 1) * (int)(row_elems * 2) + D * 2;
+    }
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(cache_b + boff), 0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(cache_b + a.plane * 2 + boff), 0, nrec, 0x00020000);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      if (kb + lr + LPR * i < kv1) {
-        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(p + (int64_t)LPR * i * row_elems);
-        bf[i] = __builtin_nontemporal_load(src);
-        bf[NLD + i] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(src) + a.plane));
-      } else {
-        bf[i] = u32x4_t{0u, 0u, 0u, 0u};
-        bf[NLD + i] = u32x4_t{0u, 0u, 0u, 0u};
-      }
+      bf[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, voff[i], 0, 2));
+      bf[NLD + i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[i], 0, 2));
     }
   };
 
@@ -257,8 +269,7 @@ __global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
   for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-  for (int p = 0; p < PF; ++p)
-    if (p < nsteps) issue(buf[p], p);
+  for (int p = 0; p < PF; ++p) issue(buf[p], p);
 
   // LDS addresses that do not change between steps
   const int vr = 4 * g + (n >> 2);                         // V row of this lane's transposing read
@@ -274,7 +285,7 @@ __global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
         *reinterpret_cast<u32x4_t*>(wl + row * RB + swz<CPR>(row, lc) * 16) = buf[p][i];
         *reinterpret_cast<u32x4_t*>(wl + (16 + row) * RB + swz<CPR>(row, lc) * 16) = buf[p][NLD + i];
       }
-      if (st + PF < nsteps) issue(buf[p], st + PF);
+      issue(buf[p], st + PF);
       const int kb = kv0 + 16 * (wave + 4 * st);
 
       // S^T (16 keys x 16 rows): lane (n, g) reg i <- key kb + 4g + i

@@ -140,29 +140,20 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
   }
 
   // ---- split-KV choice
-  // small-row kernel: a workgroup walks its range in steps of SMALL_WG_KEYS
-  // keys; tiled kernel: KEY_TILE keys per tile.  Ranges are cut on these.
   int64_t small_keys = 0, tiled_keys = 0, n_tiled = 0, n_small = 0;
   for (const Unit& u : units) {
     if (u.small) { small_keys += u.kv_end; ++n_small; }
     else { tiled_keys += u.kv_end; ++n_tiled; }
   }
   const int64_t target = PA_PLAN_TARGET_CUS;
-  int64_t small_chunk = 0, tiled_chunk = 0;
-  if (force_splits == 0) {
-    // small rows are bound by HBM: cut ranges so there are about
-    // SMALL_WGS_PER_CU workgroups per CU, but never under SMALL_MIN_CHUNK keys
-    const int64_t want = target * kSmallWgsPerCu;
-    small_chunk = std::max<int64_t>(kSmallMinChunk,
-                                    ceil_div(ceil_div(std::max<int64_t>(small_keys, 1), want),
-                                             kSmallChunkAlign) * kSmallChunkAlign);
-    // tiled rows: split only when there are too few blocks to fill the chip
-    if (n_tiled > 0 && n_tiled < target) {
-      const int64_t want_t = 2 * target;
-      tiled_chunk = std::max<int64_t>(kTiledMinChunk,
-                                      ceil_div(ceil_div(std::max<int64_t>(tiled_keys, 1), want_t),
-                                               kKeyTile) * kKeyTile);
-    }
+  int64_t tiled_chunk = 0;
+  // tiled rows (bound by the matrix cores): split only when there are too
+  // few blocks to fill the chip; cuts fall on whole key tiles
+  if (force_splits == 0 && n_tiled > 0 && n_tiled < target) {
+    const int64_t want_t = 2 * target;
+    tiled_chunk = std::max<int64_t>(kTiledMinChunk,
+                                    ceil_div(ceil_div(std::max<int64_t>(tiled_keys, 1), want_t),
+                                             kKeyTile) * kKeyTile);
   }
 
   thread_local std::vector<Item> small_items, tiled_items, reduce_items;
@@ -170,45 +161,79 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
   tiled_items.clear();
   reduce_items.clear();
   int64_t prow = 0;
+  // a unit whose range became items [first, end) of `dst`: when it is split,
+  // give every piece its partial rows and add the reduce item
+  auto finish_unit = [&](const Unit& u, std::vector<Item>& dst, size_t first) -> bool {
+    const int64_t n = (int64_t)(dst.size() - first);
+    if (n <= 1) return true;
+    for (int64_t s = 0; s < n; ++s) dst[first + s].w[6] = (int32_t)(prow + s * u.nrows);
+    reduce_items.push_back(
+        Item{{u.seq, u.kvh, u.row0, u.nrows, (int32_t)prow, (int32_t)n, 0, 0}, 0});
+    prow += n * u.nrows;
+    return prow <= INT32_MAX / 2;
+  };
+
+  // ---- small units (HBM-bound): cut into pieces so that there are about
+  // kSmallItemsPerCu workgroups per CU (each piece a multiple of 64 keys:
+  // one step of every wave, never under kSmallMinChunk); forced splits
+  // (tests) cut every unit into force_splits ranges of a multiple of 16 keys
+  if (n_small > 0) {
+    const int64_t chunk = std::max<int64_t>(
+        kSmallMinChunk,
+        ceil_div(ceil_div(std::max<int64_t>(small_keys, 1), target * kSmallItemsPerCu), 64) * 64);
+    for (const Unit& u : units) {
+      if (!u.small) continue;
+      const size_t first = small_items.size();
+      const int32_t kv = u.kv_end;
+      int32_t c = kv;
+      if (kv > 0) {
+        if (force_splits > 0) {
+          c = std::max(16, ceil_div32(ceil_div32(kv, force_splits), 16) * 16);
+        } else if (kv > chunk) {
+          const int32_t nsp = ceil_div32(kv, (int32_t)chunk);
+          c = ceil_div32(ceil_div32(kv, nsp), 64) * 64;
+        }
+      }
+      int32_t k0 = 0;
+      do {
+        const int32_t k1 = std::min(kv, k0 + std::max(c, 1));
+        small_items.push_back(
+            Item{{u.seq, u.kvh, u.row0, u.nrows, k0, k1, -1, 0}, (int64_t)(k1 - k0) * u.nrows});
+        k0 = k1;
+      } while (k0 < kv);
+      if (!finish_unit(u, small_items, first)) return PA_ERR_INVALID_ARGUMENT;
+    }
+  }
+
+  // ---- tiled units
   for (const Unit& u : units) {
-    // planner-chosen cuts fall on whole steps of the kernel; forced splits
-    // (tests) only keep ranges a multiple of 16 keys so tiny inputs still split
+    if (u.small) continue;
+    // planner-chosen cuts fall on whole key tiles; forced splits (tests)
+    // only keep ranges a multiple of 16 keys so tiny inputs still split
     // (32-bit arithmetic: key counts are below 2^30, and 64-bit divisions
     // would dominate the planner's time)
-    const int32_t align = force_splits > 0 ? 16 : (u.small ? kSmallChunkAlign : kKeyTile);
+    const int32_t align = force_splits > 0 ? 16 : kKeyTile;
     const int32_t kv = u.kv_end;
-    int32_t nsplit = 1, chunk = kv;
+    int32_t chunk = kv;
     if (kv > 0) {
       if (force_splits > 0) {
         chunk = ceil_div32(ceil_div32(kv, force_splits), align) * align;
-      } else {
-        const int64_t c = u.small ? small_chunk : tiled_chunk;
-        if (c > 0 && kv > c) {
-          // equal-sized pieces, each a multiple of the alignment
-          const int32_t n = ceil_div32(kv, (int32_t)c);
-          chunk = ceil_div32(ceil_div32(kv, n), align) * align;
-        }
+      } else if (tiled_chunk > 0 && kv > tiled_chunk) {
+        // equal-sized pieces, each a multiple of the alignment
+        const int32_t n = ceil_div32(kv, (int32_t)tiled_chunk);
+        chunk = ceil_div32(ceil_div32(kv, n), align) * align;
       }
       chunk = std::max(chunk, align);
-      nsplit = ceil_div32(kv, chunk);
     }
-    auto& dst = u.small ? small_items : tiled_items;
-    if (nsplit <= 1) {
-      Item it{{u.seq, u.kvh, u.row0, u.nrows, 0, u.kv_end, -1, 0}, (int64_t)u.kv_end * u.nrows};
-      dst.push_back(it);
-      continue;
-    }
-    const int64_t base = prow;
-    for (int64_t s = 0; s < nsplit; ++s) {
-      const int64_t k0 = s * chunk, k1 = std::min<int64_t>(u.kv_end, k0 + chunk);
-      Item it{{u.seq, u.kvh, u.row0, u.nrows, (int32_t)k0, (int32_t)k1,
-               (int32_t)(base + s * u.nrows), 0},
-              (k1 - k0) * u.nrows};
-      dst.push_back(it);
-    }
-    prow += nsplit * u.nrows;
-    if (prow > INT32_MAX / 2) return PA_ERR_INVALID_ARGUMENT;
-    reduce_items.push_back(Item{{u.seq, u.kvh, u.row0, u.nrows, (int32_t)base, (int32_t)nsplit, 0, 0}, 0});
+    const size_t first = tiled_items.size();
+    int32_t k0 = 0;
+    do {
+      const int32_t k1 = std::min(kv, k0 + chunk);
+      tiled_items.push_back(
+          Item{{u.seq, u.kvh, u.row0, u.nrows, k0, k1, -1, 0}, (int64_t)(k1 - k0) * u.nrows});
+      k0 = k1;
+    } while (k0 < kv);
+    if (!finish_unit(u, tiled_items, first)) return PA_ERR_INVALID_ARGUMENT;
   }
   const size_t n_items = small_items.size() + tiled_items.size() + reduce_items.size();
   const size_t words = PA_WORKLIST_HEADER_WORDS + n_items * PA_ITEM_WORDS;

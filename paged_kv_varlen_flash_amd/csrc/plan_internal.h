@@ -13,12 +13,13 @@ namespace pa {
 constexpr int kTiledWaves = 4;
 constexpr int kKeyTile = 64;
 constexpr int kTiledMinChunk = 256;
-// small-row kernel: 4 waves, each takes 32-key steps
+// small-row kernel: 4 waves taking 16-key steps in turn; the planner cuts
+// key ranges into pieces of at least kSmallMinChunk keys so that there are
+// about kSmallItemsPerCu workgroups per compute unit
 constexpr int kSmallWaves = 4;
-constexpr int kSmallStep = 32;
-constexpr int kSmallChunkAlign = kSmallStep * kSmallWaves;  // one step of every wave
+constexpr int kSmallStep = 16;
 constexpr int kSmallMinChunk = 256;
-constexpr int kSmallWgsPerCu = 4;
+constexpr int kSmallItemsPerCu = 4;
 
 static_assert(PA_TILED_ROWS == kTiledWaves * 32, "tiled row block");
 

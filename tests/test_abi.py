@@ -278,3 +278,21 @@ def test_plan_is_deterministic(L):
     a, _ = ops.pa_plan_varlen(p, wl.cu_seqlens_q, wl.k_lens)
     b, _ = ops.pa_plan_varlen(p, wl.cu_seqlens_q, wl.k_lens)
     assert np.array_equal(a, b)
+
+
+def test_small_items_longest_first(L):
+    """Small items (decode rows) are listed longest first, and the pieces of
+    a split unit are a multiple of 64 keys (one step of each of the kernel's
+    four waves) except the last one."""
+    wl = W.make("decode_llama8b", materialise=False)
+    p = ops.make_params(wl.B, wl.H, wl.Hkv, wl.D, wl.BS, wl.num_blocks, wl.block_table.shape[1],
+                        True, wl.scale)
+    words, info = ops.pa_plan_varlen(p, wl.cu_seqlens_q, wl.k_lens)
+    items, red = parse(words, info)
+    small = items[:info.num_small_items]
+    cost = (small[:, 5] - small[:, 4]) * small[:, 3]
+    assert np.all(np.diff(cost) <= 0)
+    assert (small[:, 5] - small[:, 4]).sum() == int(wl.k_lens.sum()) * wl.Hkv
+    for seq, kvh, row0, nrows, k0, k1, prow, _ in small:
+        if prow >= 0 and k1 != wl.k_lens[seq]:
+            assert (k1 - k0) % 64 == 0 and k0 % 64 == 0
