@@ -237,7 +237,10 @@ pa_status pa_merge_attn_states(void* out, float* out_lse,
  * then num_small_items + num_tiled_items attention items, then the reduce
  * items, PA_ITEM_WORDS words each.
  * attention item: seq, kv_head, row0, nrows, kv_begin, kv_end,
- *   partial_row (-1: write out/lse directly), 0
+ *   partial_row (-1: write out/lse directly), kind (0: small-row item of
+ *   <= PA_SMALL_MAX_ROWS rows, 1: tiled item of <= PA_TILED_ROWS rows).
+ *   When both kinds are present they are interleaved, longest estimated
+ *   time first, and run as one launch; otherwise all items are one kind.
  * reduce item: seq, kv_head, row0, nrows, partial_row0, num_splits, 0, 0
  *   (split s of the unit wrote rows partial_row0 + s * nrows ...)
  * A "row" of sequence b is (query token i, head-in-group g) -> row i*G + g,

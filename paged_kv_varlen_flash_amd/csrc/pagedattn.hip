@@ -183,21 +183,26 @@ __device__ __forceinline__ int swz(int r, int c) {
   return c ^ ((r % (CPR / 2)) * 2);
 }
 
+// LDS bytes of one small-row workgroup: four staging tiles, or the epilogue
+// merge area
 template <int D>
-__global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
+constexpr int small_lds_bytes() {
+  return (4 * SmallCfg<D>::WAVE_LDS > (4 * 16 * D + 2 * 64) * 4) ? 4 * SmallCfg<D>::WAVE_LDS
+                                                                  : (4 * 16 * D + 2 * 64) * 4;
+}
+
+template <int D>
+__device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* item, uint8_t* smem) {
   using C = SmallCfg<D>;
   constexpr int CPR = C::CPR, LPR = C::LPR, NLD = C::NLD, PF = C::PF, RB = C::RB;
   constexpr int NT = D / 32;        // QK k-steps
   constexpr int NDT = D / 16;       // 16-wide d tiles of O^T
-  constexpr int EPI_BYTES = (4 * 16 * D + 2 * 64) * 4;
-  constexpr int SMEM_BYTES = (4 * C::WAVE_LDS > EPI_BYTES) ? 4 * C::WAVE_LDS : EPI_BYTES;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int n = lane & 15, g = lane >> 4;
-  const Item it = load_item(a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS);
+  const Item it = load_item(item);
   const int t0 = ld_uniform(a.cu + it.seq);
   const int Lq = ld_uniform(a.cu + it.seq + 1) - t0;
   const int Lk = ld_uniform(a.seqused_k + it.seq);
@@ -401,6 +406,12 @@ __global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[small_lds_bytes<D>()];
+  small_body<D>(a, a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS, smem);
+}
+
 // ---------------------------------------------------------------------------
 // Tiled attention: one workgroup of 4 waves per 128-row block; wave w owns
 // rows 32w..32w+31 (lane (n = lane%32, h = lane/32) owns row n and the key
@@ -424,8 +435,15 @@ struct Bool {
   static constexpr bool value = B;
 };
 
+// LDS bytes of one tiled workgroup: two K tiles (pitch D+8) and two V tiles
+// (pitch D+32) of 64 keys
 template <int D>
-__global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_tiled_kernel(AttnArgs a) {
+constexpr int tiled_lds_bytes() {
+  return 2 * 64 * (D + 8) * 2 + 2 * 64 * (D + 32) * 2;
+}
+
+template <int D>
+__device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* item, uint8_t* smem) {
   constexpr int NKT = D / 16;       // QK k-steps (16 d each)
   constexpr int NDT = D / 32;       // 32-wide d tiles of O^T
   constexpr int KP = D + 8;
@@ -436,13 +454,15 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_tiled_kernel(Att
   static_assert(LOADS >= 1, "tile loader");
   // two K/V tile buffers: tile j is computed from buffer j%2 while tile j+1's
   // registers land in the other one
-  __shared__ __attribute__((aligned(16))) uint16_t kl[2][64 * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t vl[2][64 * VP];
+  typedef uint16_t ktile_t[64 * KP];
+  typedef uint16_t vtile_t[64 * VP];
+  ktile_t* kl = reinterpret_cast<ktile_t*>(smem);
+  vtile_t* vl = reinterpret_cast<vtile_t*>(smem + 2 * 64 * KP * 2);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
-  const Item it = load_item(a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS);
+  const Item it = load_item(item);
   const int t0 = ld_uniform(a.cu + it.seq);
   const int Lq = ld_uniform(a.cu + it.seq + 1) - t0;
   const int Lk = ld_uniform(a.seqused_k + it.seq);
@@ -670,6 +690,30 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_tiled_kernel(Att
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_tiled_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[tiled_lds_bytes<D>()];
+  tiled_body<D>(a, a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS, smem);
+}
+
+// ---------------------------------------------------------------------------
+// Mixed launch: when a batch has both decode-like and prefill rows, one grid
+// runs both kinds of item (word 7 of an item: 0 small-row, 1 tiled), in the
+// planner's longest-first order, so the HBM-bound small-row workgroups and
+// the matrix-core-bound tiled ones share the compute units instead of
+// running one kernel after the other.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_mixed_kernel(AttnArgs a) {
+  constexpr int L = small_lds_bytes<D>() > tiled_lds_bytes<D>() ? small_lds_bytes<D>() : tiled_lds_bytes<D>();
+  __shared__ __attribute__((aligned(16))) uint8_t smem[L];
+  const int32_t* item = a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS;
+  if (ld_uniform(item + 7))
+    tiled_body<D>(a, item, smem);
+  else
+    small_body<D>(a, item, smem);
+}
+
 // ---------------------------------------------------------------------------
 // Split-KV reduction: one workgroup per (reduce item, row); its 4 waves take
 // every 4th split, each lane D/64 elements of the row, and the waves'
@@ -793,12 +837,13 @@ pa_status launch_fwd(const AttnArgs& base, const pa_plan_info* plan, const int32
                      hipStream_t stream) {
   const int32_t* items = worklist + PA_WORKLIST_HEADER_WORDS;
   AttnArgs a = base;
-  if (plan->num_small_items > 0) {
-    a.items = items;
+  a.items = items;
+  if (plan->num_small_items > 0 && plan->num_tiled_items > 0) {
+    hipLaunchKernelGGL(attn_mixed_kernel<D>,
+                       dim3(plan->num_small_items + plan->num_tiled_items), dim3(256), 0, stream, a);
+  } else if (plan->num_small_items > 0) {
     hipLaunchKernelGGL(attn_small_kernel<D>, dim3(plan->num_small_items), dim3(256), 0, stream, a);
-  }
-  if (plan->num_tiled_items > 0) {
-    a.items = items + (int64_t)plan->num_small_items * PA_ITEM_WORDS;
+  } else if (plan->num_tiled_items > 0) {
     hipLaunchKernelGGL(attn_tiled_kernel<D>, dim3(plan->num_tiled_items), dim3(256), 0, stream, a);
   }
   if (plan->num_reduce_items > 0) {

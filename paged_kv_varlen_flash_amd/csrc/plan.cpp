@@ -197,8 +197,11 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
       int32_t k0 = 0;
       do {
         const int32_t k1 = std::min(kv, k0 + std::max(c, 1));
+        // cost: an estimate of the workgroup's time, comparable with the
+        // tiled items' (a small-row workgroup streams a key about as fast as
+        // a full 128-row tiled one computes it)
         small_items.push_back(
-            Item{{u.seq, u.kvh, u.row0, u.nrows, k0, k1, -1, 0}, (int64_t)(k1 - k0) * u.nrows});
+            Item{{u.seq, u.kvh, u.row0, u.nrows, k0, k1, -1, 0}, (int64_t)(k1 - k0) * PA_TILED_ROWS});
         k0 = k1;
       } while (k0 < kv);
       if (!finish_unit(u, small_items, first)) return PA_ERR_INVALID_ARGUMENT;
@@ -230,7 +233,7 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
     do {
       const int32_t k1 = std::min(kv, k0 + chunk);
       tiled_items.push_back(
-          Item{{u.seq, u.kvh, u.row0, u.nrows, k0, k1, -1, 0}, (int64_t)(k1 - k0) * u.nrows});
+          Item{{u.seq, u.kvh, u.row0, u.nrows, k0, k1, -1, 1}, (int64_t)(k1 - k0) * u.nrows});
       k0 = k1;
     } while (k0 < kv);
     if (!finish_unit(u, tiled_items, first)) return PA_ERR_INVALID_ARGUMENT;
@@ -269,8 +272,14 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
   // costs keep the (seq, kv head) order, which keeps a sequence's blocks
   // close in time and their keys warm in L2
   int32_t* dst = wl + PA_WORKLIST_HEADER_WORDS;
-  dst = emit_by_cost(small_items, dst);
-  dst = emit_by_cost(tiled_items, dst);
+  if (!small_items.empty() && !tiled_items.empty()) {
+    // one mixed launch: both kinds in one longest-first order
+    small_items.insert(small_items.end(), tiled_items.begin(), tiled_items.end());
+    dst = emit_by_cost(small_items, dst);
+  } else {
+    dst = emit_by_cost(small_items, dst);
+    dst = emit_by_cost(tiled_items, dst);
+  }
   for (const Item& it : reduce_items) {
     std::memcpy(dst, it.w, sizeof(it.w));
     dst += PA_ITEM_WORDS;

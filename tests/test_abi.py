@@ -208,8 +208,10 @@ def check_plan_covers(H, Hkv, q_lens, k_lens, causal, force_splits=0):
     items, red = parse(words, info)
     cover = {}
     small_rows = PA_SMALL = 16
-    for idx, (seq, kvh, row0, nrows, k0, k1, prow, _) in enumerate(items):
-        is_small = idx < info.num_small_items
+    assert (items[:, 7] == 0).sum() == info.num_small_items
+    assert (items[:, 7] == 1).sum() == info.num_tiled_items
+    for idx, (seq, kvh, row0, nrows, k0, k1, prow, kind) in enumerate(items):
+        is_small = kind == 0
         assert nrows <= (PA_SMALL if is_small else 128) and nrows >= 1
         for r in range(row0, row0 + nrows):
             cover.setdefault((seq, kvh, r), []).append((k0, k1, prow))
@@ -289,7 +291,7 @@ def test_small_items_longest_first(L):
                         True, wl.scale)
     words, info = ops.pa_plan_varlen(p, wl.cu_seqlens_q, wl.k_lens)
     items, red = parse(words, info)
-    small = items[:info.num_small_items]
+    small = items[items[:, 7] == 0]
     cost = (small[:, 5] - small[:, 4]) * small[:, 3]
     assert np.all(np.diff(cost) <= 0)
     assert (small[:, 5] - small[:, 4]).sum() == int(wl.k_lens.sum()) * wl.Hkv
