@@ -577,15 +577,15 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
     // raw scores; the scale (> 0) is applied inside the exponent, so the max
     // is taken on raw scores and scaled once
     float x[32];
+    // the last visible key of this lane's row, relative to the lane's first
+    // key j0 + 4h, so that each element compares a compile-time offset
+    const int lim = min(kv1 - 1, row_limit) - j0 - 4 * h;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float v = s[u][i];
-        if constexpr (MASKED) {
-          const int key = j0 + 32 * u + 8 * (i >> 2) + 4 * h + (i & 3);
-          v = (key >= kv1 || key > row_limit) ? kNegInf : v;
-        }
+        if constexpr (MASKED) v = (32 * u + 8 * (i >> 2) + (i & 3) > lim) ? kNegInf : v;
         x[16 * u + i] = v;
       }
     float mx = x[0];
@@ -601,13 +601,13 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
       m_run = m_new;
     }
     const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
-    float ps = 0.f;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};     // four independent partial sums
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], a.scale_log2, neg_m));
-      ps += x[i];
+      ps[i & 3] += x[i];
     }
-    l_run += ps;
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
     // P^T operands for the four 16-key steps: step ks = 2u + half uses
     // regs 8*half .. 8*half+7 of tile u
     bf16x8_t pb[4];
