@@ -39,6 +39,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -58,6 +59,18 @@ __device__ __forceinline__ bf16x8_t pack_bf16x8(const float* p) {
   w.z = pack_bf16x2(p[4], p[5]);
   w.w = pack_bf16x2(p[6], p[7]);
   return __builtin_bit_cast(bf16x8_t, w);
+}
+
+// acc + the sum of the bf16 values packed in w (v_dot2 with ones: the bf16
+// values are exact in fp32, so this sums exactly the probabilities that the
+// PV product multiplies)
+__device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                          __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
+}
+__device__ __forceinline__ float add_bf16x8(bf16x8_t p, float acc) {
+  const u32x4_t w = __builtin_bit_cast(u32x4_t, p);
+  return add_bf16x2(w[3], add_bf16x2(w[2], add_bf16x2(w[1], add_bf16x2(w[0], acc))));
 }
 
 __device__ __forceinline__ bf16x8_t ld16(const uint16_t* p) {
@@ -165,7 +178,6 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
 // Item key ranges start on a multiple of 16, and block_size is a multiple
 // of 16, so the 16 keys of a step lie in one cache block.
 // ---------------------------------------------------------------------------
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct SmallCfg {
@@ -187,8 +199,8 @@ __device__ __forceinline__ int swz(int r, int c) {
 // merge area
 template <int D>
 constexpr int small_lds_bytes() {
-  return (4 * SmallCfg<D>::WAVE_LDS > (4 * 16 * D + 2 * 64) * 4) ? 4 * SmallCfg<D>::WAVE_LDS
-                                                                  : (4 * 16 * D + 2 * 64) * 4;
+  return (4 * SmallCfg<D>::WAVE_LDS > (4 * 16 * D + 3 * 64) * 4) ? 4 * SmallCfg<D>::WAVE_LDS
+                                                                  : (4 * 16 * D + 3 * 64) * 4;
 }
 
 template <int D>
@@ -268,7 +280,9 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
     }
   };
 
-  float m_run = kNegInf, l_run = 0.f;
+  // l_run sums the fp32 probabilities (for the LSE), lr_run the bf16-rounded
+  // ones that the PV product multiplies (for the normalisation of O)
+  float m_run = kNegInf, l_run = 0.f, lr_run = 0.f;
   f32x4_t o[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -326,6 +340,7 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
       uint2 pw;
       pw.x = pack_bf16x2(pr[0], pr[1]);
       pw.y = pack_bf16x2(pr[2], pr[3]);
+      lr_run = add_bf16x2(pw.y, add_bf16x2(pw.x, lr_run * alpha));
       const bf16x4_t pb = __builtin_bit_cast(bf16x4_t, pw);
       // O^T += V^T P^T; lane (s, g) of each 16-lane group reads 4 d of key
       // 4g + s/4, so lane s receives d = 16dt + s of keys 4g..4g+3
@@ -342,10 +357,13 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
   // ---- merge the four waves' partial states through LDS
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
+  lr_run += __shfl_xor(lr_run, 16);
+  lr_run += __shfl_xor(lr_run, 32);
   __syncthreads();
   float* so = reinterpret_cast<float*>(smem);
   float* sm = so + 4 * 16 * D;
   float* sl = sm + 64;
+  float* sr = sl + 64;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -353,6 +371,7 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
   if (g == 0) {
     sm[wave * 16 + n] = m_run;
     sl[wave * 16 + n] = l_run;
+    sr[wave * 16 + n] = lr_run;
   }
   __syncthreads();
   constexpr int DPT = D / 16;  // d elements per thread in the epilogue
@@ -361,15 +380,16 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
     float M = kNegInf;
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w * 16 + er]);
-    float wt[4], L = 0.f;
+    float wt[4], L = 0.f, Lr = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const float mw = sm[w * 16 + er];
       wt[w] = (M == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
       L += wt[w] * sl[w * 16 + er];
+      Lr += wt[w] * sr[w * 16 + er];
     }
     const bool empty = !(L > 0.f);
-    const float inv = empty ? 0.f : 1.f / L;
+    const float inv = empty ? 0.f : 1.f / Lr;
     const float lse_v = empty ? kNegInf : (M + __log2f(L)) * kLn2;
     float acc[DPT];
 #pragma unroll
@@ -546,7 +566,9 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
     }
   };
 
-  float m_run = kNegInf, l_run = 0.f;
+  // l_run sums the fp32 probabilities (for the LSE), lr_run the bf16-rounded
+  // ones that the PV product multiplies (for the normalisation of O)
+  float m_run = kNegInf, l_run = 0.f, lr_run = 0.f;
   f32x16_t o[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
@@ -596,6 +618,7 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
       const float m_new = fmaxf(m_run, mx);
       const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
+      lr_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
       m_run = m_new;
@@ -612,7 +635,10 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
     // regs 8*half .. 8*half+7 of tile u
     bf16x8_t pb[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) pb[ks] = pack_bf16x8(x + 8 * ks);
+    for (int ks = 0; ks < 4; ++ks) {
+      pb[ks] = pack_bf16x8(x + 8 * ks);
+      lr_run = add_bf16x8(pb[ks], lr_run);
+    }
     // O^T += V^T P^T; A operand lane (m = d row, h) slots: keys kb+4h+0..3,
     // kb+8+4h+0..3 with kb = 16*ks, read transposed from LDS per 16-lane group
 #pragma unroll
@@ -659,9 +685,10 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
   }
 
   l_run += __shfl_xor(l_run, 32);
+  lr_run += __shfl_xor(lr_run, 32);
   if (!row_ok) return;
   const bool empty = !(l_run > 0.f);
-  const float inv = empty ? 0.f : 1.f / l_run;
+  const float inv = empty ? 0.f : 1.f / lr_run;
   const float lse_v = empty ? kNegInf : (m_run + __log2f(l_run)) * kLn2;
   // lane (n, h) reg i of tile dt holds O^T[d = 32dt + 8(i/4) + 4h + i%4][row n]
   if (it.prow < 0) {

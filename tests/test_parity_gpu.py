@@ -161,6 +161,36 @@ def test_fuzz(seed):
     say(f"fuzz seed={seed} D={spec.head_size} H={spec.num_heads} Hkv={spec.num_kv_heads} "
         f"BS={spec.block_size} causal={spec.causal} seqs={spec.fixed}")
     rng = np.random.default_rng(seed)
+    force = int(rng.choice([0, 0, 2, 5]))
+    _check_case(spec, rng, force, f"fuzz{seed}")
+
+
+# Batches whose every sequence has more than 16 rows (query tokens x heads
+# per KV head), so that the launch holds tiled items only: ragged tails,
+# rows that see no key (Lq > Lk under the causal mask), split key ranges.
+PREFILL_ONLY = [
+    # D, G, Hkv, BS, causal, (Lq, Lk) per sequence, forced splits
+    (128, 4, 2, 32, True, ((300, 300), (77, 200), (5, 5), (129, 1000)), 0),
+    (128, 4, 2, 16, False, ((64, 64), (33, 97), (200, 450)), 3),
+    (64, 8, 1, 48, True, ((40, 40), (17, 300), (250, 260)), 0),
+    (64, 2, 3, 64, False, ((100, 130), (9, 9)), 2),
+    (128, 1, 2, 16, True, ((600, 600), (20, 10)), 5),
+    (256, 4, 1, 32, True, ((70, 70), (33, 180)), 0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(PREFILL_ONLY)))
+def test_prefill_only(case):
+    D, G, Hkv, BS, causal, seqs, force = PREFILL_ONLY[case]
+    spec = W.Spec(name=f"prefill_only{case}", num_heads=G * Hkv, num_kv_heads=Hkv, head_size=D,
+                  block_size=BS, causal=causal, seed=7000 + case, fixed=seqs, min_num_blocks=3)
+    say(f"prefill-only case={case} D={D} G={G} Hkv={Hkv} BS={BS} causal={causal} seqs={seqs} "
+        f"force={force}")
+    plan = _check_case(spec, np.random.default_rng(7000 + case), force, f"prefill_only{case}")
+    assert plan.info.num_small_items == 0 and plan.info.num_tiled_items > 0
+
+
+def _check_case(spec, rng, force, label):
     q_lens = np.array([a for a, _ in spec.fixed], np.int32)
     k_lens = np.array([b for _, b in spec.fixed], np.int32)
     B, H, Hkv, D, BS = len(q_lens), spec.num_heads, spec.num_kv_heads, spec.head_size, spec.block_size
@@ -181,7 +211,6 @@ def test_fuzz(seed):
     for b in range(B):
         for j in range(k_lens[b], nblk[b] * BS):
             cache[:, bt[b, j // BS], j % BS] = W.SENTINEL
-    force = int(rng.choice([0, 0, 2, 5]))
     scale = np.float32(1.0 / np.sqrt(D))
     p = ops.make_params(B, H, Hkv, D, BS, NB, MB, spec.causal, scale)
     plan = ops.VarlenPlan(p, cu, k_lens, force)
@@ -194,7 +223,8 @@ def test_fuzz(seed):
     torch.cuda.synchronize()
     ref_out, ref_lse = OA.varlen_attention(q, cache, cu, k_lens, bt, scale, spec.causal)
     compare(out.float().cpu().numpy(), lse.cpu().numpy(), ref_out, ref_lse,
-            label=f"fuzz{seed} force={force}")
+            label=f"{label} force={force}")
+    return plan
 
 
 # ------------------------------------------------------------ merge
