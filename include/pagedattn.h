@@ -241,7 +241,8 @@ pa_status pa_merge_attn_states(void* out, float* out_lse,
  *   <= PA_SMALL_MAX_ROWS rows, 1: tiled item of <= PA_TILED_ROWS rows).
  *   When both kinds are present they are interleaved, longest estimated
  *   time first, and run as one launch; otherwise all items are one kind.
- * reduce item: seq, kv_head, row0, nrows, partial_row0, num_splits, 0, 0
+ * reduce item: seq, kv_head, row0, nrows, partial_row0, num_splits,
+ *   first token of the sequence (cu_seqlens_q[seq]), 0
  *   (split s of the unit wrote rows partial_row0 + s * nrows ...)
  * A "row" of sequence b is (query token i, head-in-group g) -> row i*G + g,
  * G = H / Hkv; kv_head's query heads are kv_head*G .. kv_head*G + G-1.    */

@@ -743,65 +743,72 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_mixed_kernel(Att
 
 // ---------------------------------------------------------------------------
 // Split-KV reduction: one workgroup per (reduce item, row); its 4 waves take
-// every 4th split, each lane D/64 elements of the row, and the waves'
-// partial sums meet in LDS.  Partials hold O normalised by its own row sum
-// and the natural-log lse of that split.
+// every 4th split, each lane D/64 elements of the row.  Partials hold O
+// normalised by its own row sum and the natural-log lse of that split; a
+// wave merges its splits online (running max, rescaled sum), loading a
+// split's lse and O together, and the 4 waves' states meet in LDS.  The item
+// carries the sequence's first token and its rows are all valid (the
+// planner clips them), so the only loads on the way are the partials.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void split_reduce_kernel(
     const int32_t* __restrict__ ritems, const float* __restrict__ part_o,
-    const float* __restrict__ part_lse, const int32_t* __restrict__ cu, uint16_t* __restrict__ out,
-    float* __restrict__ lse, int H, int G) {
+    const float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse, int H,
+    int G) {
   constexpr int EPL = D / 64;
   static_assert(EPL >= 1, "split reduce");
   __shared__ float s_m[4], s_l[4];
   __shared__ __attribute__((aligned(16))) float s_o[4][D];
   const int32_t* p = ritems + (int64_t)blockIdx.x * PA_ITEM_WORDS;
-  const int seq = ld_uniform(p), kvh = ld_uniform(p + 1), row0 = ld_uniform(p + 2);
+  const int kvh = ld_uniform(p + 1), row0 = ld_uniform(p + 2);
   const int prow_n = ld_uniform(p + 3), prow0 = ld_uniform(p + 4), nsplit = ld_uniform(p + 5);
+  const int t0 = ld_uniform(p + 6);
   const int row = blockIdx.y;
-  const int t0 = ld_uniform(cu + seq);
-  const int Lq = ld_uniform(cu + seq + 1) - t0;
-  const int nrows = min(prow_n, Lq * G - row0);
-  if (row >= nrows) return;
+  if (row >= prow_n) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-  float M = kNegInf;
-  for (int s = threadIdx.x; s < nsplit; s += 256) M = fmaxf(M, part_lse[prow0 + s * prow_n + row]);
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) M = wave_max_xor(M, m);
-  if (lane == 0) s_m[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
-
+  // online merge over this wave's splits, in the log2 domain
+  float m = kNegInf, L = 0.f;
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  float L = 0.f;
-  if (M != kNegInf) {
 #pragma unroll 4
-    for (int s = wave; s < nsplit; s += 4) {
-      const int pr = prow0 + s * prow_n + row;
-      const float ls = part_lse[pr];
-      const float w = (ls == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((ls - M) * kLog2e);
-      L += w;
-      const float* src = part_o + (int64_t)pr * D + lane * EPL;
+  for (int s = wave; s < nsplit; s += 4) {
+    const int pr = prow0 + s * prow_n + row;
+    const float ls = part_lse[pr] * kLog2e;
+    float v[EPL];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] += w * src[e];
-    }
+    for (int e = 0; e < EPL; ++e) v[e] = part_o[(int64_t)pr * D + lane * EPL + e];
+    const float m_new = fmaxf(m, ls);
+    if (m_new == kNegInf) continue;   // nothing seen yet: both sides empty
+    const float a = __builtin_amdgcn_exp2f(m - m_new);   // 0 when m = -inf
+    const float b = __builtin_amdgcn_exp2f(ls - m_new);  // 0 when ls = -inf
+    L = L * a + b;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * a + b * v[e];
+    m = m_new;
   }
 #pragma unroll
   for (int e = 0; e < EPL; ++e) s_o[wave][lane * EPL + e] = acc[e];
-  if (lane == 0) s_l[wave] = L;
+  if (lane == 0) {
+    s_m[wave] = m;
+    s_l[wave] = L;
+  }
   __syncthreads();
   if (wave != 0) return;
-  L = (s_l[0] + s_l[1]) + (s_l[2] + s_l[3]);
-  const bool empty = !(L > 0.f);
-  const float inv = empty ? 0.f : 1.f / L;
+  const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  float w[4], Lt = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    w[k] = (s_m[k] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(s_m[k] - M);
+    Lt += w[k] * s_l[k];
+  }
+  const bool empty = !(Lt > 0.f);
+  const float inv = empty ? 0.f : 1.f / Lt;
 #pragma unroll
   for (int e = 0; e < EPL; ++e)
-    acc[e] = ((s_o[0][lane * EPL + e] + s_o[1][lane * EPL + e]) +
-              (s_o[2][lane * EPL + e] + s_o[3][lane * EPL + e])) * inv;
+    acc[e] = ((w[0] * s_o[0][lane * EPL + e] + w[1] * s_o[1][lane * EPL + e]) +
+              (w[2] * s_o[2][lane * EPL + e] + w[3] * s_o[3][lane * EPL + e])) * inv;
   const int rr = row0 + row;
   const int tok = rr / G;
   const int head = kvh * G + (rr - tok * G);
@@ -814,7 +821,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(
     for (int e = 0; e < EPL; e += 2)
       *reinterpret_cast<uint32_t*>(op + e) = pack_bf16x2(acc[e], acc[e + 1]);
   }
-  if (lane == 0 && lse) lse[orow] = empty ? kNegInf : M + __logf(L);
+  if (lane == 0 && lse) lse[orow] = empty ? kNegInf : (M + __log2f(Lt)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -878,7 +885,7 @@ pa_status launch_fwd(const AttnArgs& base, const pa_plan_info* plan, const int32
         items + (int64_t)(plan->num_small_items + plan->num_tiled_items) * PA_ITEM_WORDS;
     hipLaunchKernelGGL(split_reduce_kernel<D>, dim3(plan->num_reduce_items, plan->max_reduce_rows),
                        dim3(256), 0, stream,
-                       r, base.part_o, base.part_lse, base.cu, base.out, base.lse, base.H, base.G);
+                       r, base.part_o, base.part_lse, base.out, base.lse, base.H, base.G);
   }
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

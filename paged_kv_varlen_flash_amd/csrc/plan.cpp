@@ -168,7 +168,7 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
     if (n <= 1) return true;
     for (int64_t s = 0; s < n; ++s) dst[first + s].w[6] = (int32_t)(prow + s * u.nrows);
     reduce_items.push_back(
-        Item{{u.seq, u.kvh, u.row0, u.nrows, (int32_t)prow, (int32_t)n, 0, 0}, 0});
+        Item{{u.seq, u.kvh, u.row0, u.nrows, (int32_t)prow, (int32_t)n, cu[u.seq], 0}, 0});
     prow += n * u.nrows;
     return prow <= INT32_MAX / 2;
   };

@@ -237,8 +237,10 @@ def check_plan_covers(H, Hkv, q_lens, k_lens, causal, force_splits=0):
                     assert ranges[0][2] == -1
     assert not cover, "items for rows that do not exist"
     # reduce items point at the split items' partial rows
-    for seq, kvh, row0, nrows, prow0, nsplit, _, _ in red:
+    for seq, kvh, row0, nrows, prow0, nsplit, tok0, _ in red:
         assert nsplit >= 2
+        assert tok0 == cu[seq]                       # first token of the sequence
+        assert row0 + nrows <= q_lens[seq] * G       # rows are clipped by the planner
         for s in range(nsplit):
             assert prow0 + s * nrows in seen_prow
     assert info.num_partial_rows == (max(seen_prow) + 1 if seen_prow else 0) or \
