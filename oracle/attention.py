@@ -119,16 +119,27 @@ def _softmax_rows(s: np.ndarray, vis: np.ndarray, v: np.ndarray):
 
 def varlen_attention(q: np.ndarray, kv_cache: np.ndarray, cu_seqlens_q: np.ndarray,
                      seqused_k: np.ndarray, block_table: np.ndarray, scale,
-                     causal: bool, num_kv_heads: int = None):
+                     causal: bool, num_kv_heads: int = None, k_scale=None, v_scale=None):
     """Paged varlen (GQA, optionally bottom-right causal) attention.
 
-    q: bf16 bits [T, H, D]; kv_cache: bf16 bits [2, NB, BS, Hkv, D];
+    q: bf16 bits [T, H, D]; kv_cache: bf16 bits (uint16) [2, NB, BS, Hkv, D],
+    or E4M3 codes (uint8) of the same shape together with the per-KV-head
+    fp32 dequantisation scales k_scale[Hkv], v_scale[Hkv] (key/value =
+    E4M3 value * scale, see oracle.fp8);
     cu_seqlens_q: [B+1]; seqused_k: [B]; block_table: [B, max_blocks];
     scale: the fp32 softmax scale (promoted exactly to fp64).
     Returns out float64 [T, H, D] and lse float64 [T, H] (natural log)."""
     T, H, D = q.shape
     Hkv = kv_cache.shape[3] if num_kv_heads is None else num_kv_heads
     scale = float(np.float32(scale))
+    fp8 = np.asarray(kv_cache).dtype == np.uint8
+    if fp8:
+        from .fp8 import e4m3_to_f64
+        ks = np.asarray(k_scale, dtype=np.float32).astype(np.float64)
+        vs = np.asarray(v_scale, dtype=np.float32).astype(np.float64)
+        widen = lambda x, sc: e4m3_to_f64(x) * sc[None, :, None]
+    elif k_scale is not None or v_scale is not None:
+        raise ValueError("scales apply to an E4M3 (uint8) cache only")
     qf = bf16_to_f64(q)
     out = np.zeros((T, H, D), dtype=np.float64)
     lse = np.full((T, H), NEG_INF, dtype=np.float64)
@@ -139,7 +150,10 @@ def varlen_attention(q: np.ndarray, kv_cache: np.ndarray, cu_seqlens_q: np.ndarr
         if Lq == 0:
             continue
         Kb, Vb = gather_kv(kv_cache, np.asarray(block_table[b]), Lk)
-        K, V = bf16_to_f64(Kb), bf16_to_f64(Vb)
+        if fp8:
+            K, V = widen(Kb, ks), widen(Vb, vs)
+        else:
+            K, V = bf16_to_f64(Kb), bf16_to_f64(Vb)
         vis = _visible(Lq, Lk, causal)
         for h in range(H):
             kvh = _kv_head(h, H, Hkv)

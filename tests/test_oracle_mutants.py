@@ -103,3 +103,80 @@ def test_mutant_is_caught(name, monkeypatch):
         except (AssertionError, IndexError, ValueError):
             caught.append(pin.__name__)
     assert caught, f"no pin catches mutant {name}"
+
+
+# ------------------------------------------------------------ FP8 (E4M3) path
+import oracle.fp8 as OF8
+import oracle_pins_fp8
+
+_orig_dec = OF8.e4m3_to_f64
+_orig_enc = OF8.f32_to_e4m3
+_orig_quant = OF8.quantize
+
+
+def _dec_bias8(codes):
+    v = _orig_dec(codes)
+    return v / 2.0
+
+
+def _dec_no_subnormals(codes):
+    c = np.asarray(codes, dtype=np.uint8)
+    v = _orig_dec(c)
+    e = (c.astype(np.int64) >> 3) & 0xF
+    m = c.astype(np.int64) & 7
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    return np.where(e == 0, sign * (1 + m / 8.0) * 2.0 ** -7, v)
+
+
+def _enc_ties_away(x):
+    x = np.asarray(x, dtype=np.float32)
+    out = _orig_enc(x)
+    # on an exact midpoint, step the even pick away from zero when it went down
+    up = _orig_enc(x * np.float32(1 + 2.0 ** -22))
+    mid = (out != up) & (np.abs(_orig_dec(out)) < np.abs(x.astype(np.float64)))
+    return np.where(mid, up, out)
+
+
+def _enc_no_saturation(x):
+    x = np.asarray(x, dtype=np.float32)
+    out = _orig_enc(x)
+    big = np.abs(x) > 448
+    return np.where(big, (out | 0x7F).astype(np.uint8), out)
+
+
+def _quant_multiply(bits, scale):
+    return _orig_quant(bits, 1.0 / float(np.float32(scale)))
+
+
+def _attn_k_scale_ignored(*args, k_scale=None, v_scale=None, **kw):
+    if k_scale is not None:
+        k_scale = np.ones_like(np.asarray(k_scale, dtype=np.float32))
+    return _orig_varlen(*args, k_scale=k_scale, v_scale=v_scale, **kw)
+
+
+def _attn_scales_swapped(*args, k_scale=None, v_scale=None, **kw):
+    return _orig_varlen(*args, k_scale=v_scale, v_scale=k_scale, **kw)
+
+
+FP8_MUTANTS = {
+    "e4m3_bias_8": (OF8, "e4m3_to_f64", _dec_bias8),
+    "e4m3_no_subnormals": (OF8, "e4m3_to_f64", _dec_no_subnormals),
+    "e4m3_ties_away": (OF8, "f32_to_e4m3", _enc_ties_away),
+    "e4m3_no_saturation": (OF8, "f32_to_e4m3", _enc_no_saturation),
+    "quantize_multiplies": (OF8, "quantize", _quant_multiply),
+    "k_scale_ignored": (OA, "varlen_attention", _attn_k_scale_ignored),
+    "k_v_scales_swapped": (OA, "varlen_attention", _attn_scales_swapped),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTANTS))
+def test_fp8_mutant_is_caught(name, monkeypatch):
+    mod, attr, fn = FP8_MUTANTS[name]
+    monkeypatch.setattr(mod, attr, fn)
+    caught = []
+    for pin in oracle_pins_fp8.ALL_PINS:
+        try:
+            pin()
+        except (AssertionError, IndexError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches mutant {name}"
