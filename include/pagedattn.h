@@ -211,6 +211,50 @@ pa_status pa_varlen_fwd(const pa_attn_params* p, const pa_plan_info* plan,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * FP8 KV cache.  The pages list an fp8 / fp8_e4m3 KV cache with per-head
+ * quantisation scales among the FlashAttention-3 and FlashInfer backend
+ * features ("FlashAttention 在 vLLM 中的实现分析", the backend section and its
+ * feature table; the backend-abstraction page, kv_cache_dtype) without a
+ * formula; these two calls take the plain reading:
+ *   format  OCP 8-bit float E4M3 (1 sign, 4 exponent bits with bias 7,
+ *           3 mantissa bits, subnormals, no infinities, S.1111.111 = NaN,
+ *           largest finite 448), one byte per element, same (2, NB, BS, Hkv,
+ *           D) layout as the bf16 cache;
+ *   write   code = E4M3(fp32(x) / k_scale[h]) (v_scale[h] for values), the
+ *           division in IEEE fp32, rounding to nearest with ties to the even
+ *           code, saturating to +-448, NaN -> 0x7F;
+ *   read    key = E4M3 value * k_scale[h], value = E4M3 value * v_scale[h].
+ *
+ * pa_reshape_and_cache_fp8: as pa_reshape_and_cache, into an E4M3 cache.
+ *   kv_cache          device uint8 (2, NB, BS, Hkv, D), updated in place
+ *   k_scale, v_scale  device fp32 [num_kv_heads], > 0 and finite
+ *   head_size         a multiple of 16
+ * Same errors as pa_reshape_and_cache.
+ * ------------------------------------------------------------------------ */
+pa_status pa_reshape_and_cache_fp8(const void* key, const void* value,
+                                   int64_t key_row_stride, int64_t value_row_stride,
+                                   void* kv_cache, const int64_t* slot_mapping,
+                                   const float* k_scale, const float* v_scale,
+                                   int32_t num_tokens, int32_t num_kv_heads, int32_t head_size,
+                                   int32_t num_blocks, int32_t block_size, hipStream_t stream);
+
+/* pa_varlen_fwd_fp8: pa_varlen_fwd over an E4M3 cache (uint8, same layout),
+ * with k_scale / v_scale the device fp32 [num_kv_heads] scales the cache was
+ * written with.  Plan, work list and workspace are those of pa_varlen_fwd
+ * (the same pa_plan_varlen call); q, out and lse are unchanged.  K and V
+ * are widened to bf16 exactly; the scales are applied in fp32 (k_scale to
+ * the scores, v_scale to the output).  Same errors as pa_varlen_fwd, and
+ * PA_ERR_INVALID_ARGUMENT for a NULL scale pointer. */
+pa_status pa_varlen_fwd_fp8(const pa_attn_params* p, const pa_plan_info* plan,
+                            const int32_t* worklist,
+                            const void* q, const void* kv_cache,
+                            const int32_t* cu_seqlens_q, const int32_t* seqused_k,
+                            const int32_t* block_table,
+                            const float* k_scale, const float* v_scale,
+                            int32_t num_tokens, void* out, float* lse,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * pa_merge_attn_states -- LSE-weighted merge of two partial attentions over
  * disjoint key sets (the cascade's third step, "FlashAttention 在 vLLM 中的
  * 实现分析" section 6.3, and the merge_attn_states helper of section 8.2):

@@ -73,6 +73,42 @@ __device__ __forceinline__ float add_bf16x8(bf16x8_t p, float acc) {
   return add_bf16x2(w[3], add_bf16x2(w[2], add_bf16x2(w[1], add_bf16x2(w[0], acc))));
 }
 
+// 16 E4M3 codes (one 16-byte load) -> 16 bf16 values in two 16-byte chunks.
+// Exact: every E4M3 value is a bf16 value, and the conversion scale is 1.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+__device__ __forceinline__ void e4m3x16_to_bf16(u32x4_t w, u32x4_t& lo, u32x4_t& hi) {
+  lo = u32x4_t{e4m3x2_to_bf16x2<false>(w[0]), e4m3x2_to_bf16x2<true>(w[0]),
+               e4m3x2_to_bf16x2<false>(w[1]), e4m3x2_to_bf16x2<true>(w[1])};
+  hi = u32x4_t{e4m3x2_to_bf16x2<false>(w[2]), e4m3x2_to_bf16x2<true>(w[2]),
+               e4m3x2_to_bf16x2<false>(w[3]), e4m3x2_to_bf16x2<true>(w[3])};
+}
+
+// fp32 -> E4M3 code (OCP E4M3: bias 7, subnormals, S.1111.111 = NaN, largest
+// finite 448): nearest value, ties to the even code, saturating at +-448,
+// NaN -> 0x7F.  Written out in integer steps so that the result does not
+// depend on a conversion instruction's rounding or clamping mode.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, x);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t a = b & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;               // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;       // |x| >= 448, infinities: saturate
+  if (a < 0x3c800000u) {                           // |x| < 2^-6: multiples of 2^-9
+    const float f = __builtin_bit_cast(float, a) * 512.0f;   // exact
+    return sign | (uint32_t)__builtin_rintf(f);    // round half to even; 8 = 2^-6
+  }
+  const uint32_t e = (a >> 23) - 127u + 7u;        // biased E4M3 exponent, 1..15
+  const uint32_t mant = a & 0x7fffffu;
+  uint32_t q = mant >> 20;
+  const uint32_t rem = mant & 0xfffffu;
+  if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;   // q = 8 carries
+  const uint32_t code = (e << 3) + q;
+  return sign | (code > 0x7eu ? 0x7eu : code);
+}
+
 __device__ __forceinline__ bf16x8_t ld16(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
 }
@@ -103,6 +139,11 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
 __device__ __forceinline__ int32_t ld_uniform(const int32_t* p) {
   typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
   return *(const_i32_ptr)(reinterpret_cast<uintptr_t>(p));
+}
+
+__device__ __forceinline__ float ld_uniform(const float* p) {
+  typedef const __attribute__((address_space(4))) float* const_f32_ptr;
+  return *(const_f32_ptr)(reinterpret_cast<uintptr_t>(p));
 }
 
 struct Item {
@@ -136,6 +177,8 @@ struct AttnArgs {
   int H, Hkv, G, BS, MB, bt_stride, causal;
   int bs_log2;        // log2(BS) when BS is a power of two, else -1
   float scale_log2;   // scale * log2(e)
+  const float* k_scale;   // E4M3 cache: per-KV-head dequantisation scales
+  const float* v_scale;
 };
 
 // ---------------------------------------------------------------------------
@@ -157,6 +200,39 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   const uint16_t* src = which ? value + t * value_stride : key + t * key_stride;
   uint16_t* dst = cache + (which ? plane : 0) + slot * row_elems;
   reinterpret_cast<uint4*>(dst)[c] = reinterpret_cast<const uint4*>(src)[c];
+}
+
+// ---------------------------------------------------------------------------
+// reshape_and_cache into an E4M3 cache: one thread per 16 output bytes (16
+// elements of one token's K or V row); code = E4M3(x / scale[kv head]), the
+// division in IEEE fp32.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
+    const uint16_t* __restrict__ key, const uint16_t* __restrict__ value, int64_t key_stride,
+    int64_t value_stride, uint8_t* __restrict__ cache, const int64_t* __restrict__ slot_mapping,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale, int64_t total_chunks,
+    int32_t chunks_per_row, int32_t chunks_per_head, int64_t row_elems, int64_t plane) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= total_chunks) return;
+  const int64_t tw = gid / chunks_per_row;      // token * 2 + which
+  const int32_t c = (int32_t)(gid - tw * chunks_per_row);
+  const int64_t t = tw >> 1;
+  const int which = (int)(tw & 1);
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0) return;
+  const uint16_t* src = (which ? value + t * value_stride : key + t * key_stride) + c * 16;
+  const float sc = (which ? v_scale : k_scale)[c / chunks_per_head];
+  const uint4 w0 = reinterpret_cast<const uint4*>(src)[0];
+  const uint4 w1 = reinterpret_cast<const uint4*>(src)[1];
+  const uint32_t in[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  uint32_t o[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const uint32_t bits = (k & 1) ? (in[k >> 1] & 0xffff0000u) : (in[k >> 1] << 16);
+    o[k >> 2] |= f32_to_e4m3(__builtin_bit_cast(float, bits) / sc) << (8 * (k & 3));
+  }
+  uint8_t* dst = cache + (which ? plane : 0) + slot * row_elems + (int64_t)c * 16;
+  *reinterpret_cast<uint4*>(dst) = uint4{o[0], o[1], o[2], o[3]};
 }
 
 // ---------------------------------------------------------------------------
@@ -203,10 +279,22 @@ constexpr int small_lds_bytes() {
                                                                   : (4 * 16 * D + 3 * 64) * 4;
 }
 
-template <int D>
+// loads of one key row: D*ES bytes in 16-byte chunks (ES = 1 for an E4M3
+// cache, whose 16-byte chunk becomes two bf16 chunks in LDS)
+template <int D, bool FP8>
+struct SmallLoad {
+  static constexpr int ES = FP8 ? 1 : 2;
+  static constexpr int CPR = D * ES / 16;    // 16-byte chunks per key row
+  static constexpr int LPR = 64 / CPR;       // key rows per wave load instruction
+  static constexpr int NLD = 16 / LPR;       // load instructions per plane per step
+};
+
+template <int D, bool FP8>
 __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* item, uint8_t* smem) {
   using C = SmallCfg<D>;
-  constexpr int CPR = C::CPR, LPR = C::LPR, NLD = C::NLD, PF = C::PF, RB = C::RB;
+  using LD = SmallLoad<D, FP8>;
+  constexpr int CPR = C::CPR, PF = C::PF, RB = C::RB;
+  constexpr int LPR = LD::LPR, NLD = LD::NLD, ES = LD::ES;
   constexpr int NT = D / 32;        // QK k-steps
   constexpr int NDT = D / 16;       // 16-wide d tiles of O^T
 
@@ -228,6 +316,10 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
   const int tok = r / G;
   const int head = it.kvh * G + (r - tok * G);
   const int row_limit = a.causal ? tok + Lk - Lq : INT_MAX;
+  // an E4M3 cache holds K / k_scale and V / v_scale of each KV head: the
+  // scores take k_scale inside the exponent's factor, O takes v_scale at the end
+  const float sl2 = FP8 ? a.scale_log2 * ld_uniform(a.k_scale + it.kvh) : a.scale_log2;
+  const float vsc = FP8 ? ld_uniform(a.v_scale + it.kvh) : 1.f;
 
   // Q^T operand: k-step t, slot j <-> d = 32t + 8g + j
   bf16x8_t qf[NT];
@@ -241,7 +333,7 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
   }
 
   // loader geometry: this lane reads chunk lc of rows lr + LPR*i
-  const int lr = lane / CPR, lc = lane % CPR;
+  const int lr = lane / LD::CPR, lc = lane % LD::CPR;
   const int64_t row_elems = (int64_t)a.Hkv * D;
   const int32_t* btrow = a.block_table + (int64_t)it.seq * a.bt_stride;
   uint8_t* wl = smem + wave * C::WAVE_LDS;       // K rows [0,16), V rows [16,32)
@@ -253,10 +345,10 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
   // range) read as zero without touching memory, so every step issues the
   // same loads and the wait before each step counts exactly the later steps'
   // loads still in flight
-  const int64_t kv_bytes = (int64_t)it.kvh * D * 2;
+  const int64_t kv_bytes = (int64_t)it.kvh * D * ES;
   int voff[NLD];
 #pragma unroll
-  for (int i = 0; i < NLD; ++i) voff[i] = (lr + LPR * i) * (int)(row_elems * 2) + lc * 16;
+  for (int i = 0; i < NLD; ++i) voff[i] = (lr + LPR * i) * (int)(row_elems * ES) + lc * 16;
   const uint8_t* cache_b = reinterpret_cast<const uint8_t*>(a.cache);
   auto issue = [&](u32x4_t* bf, int st) {
     const int kb = kv0 + 16 * (wave + 4 * st);
@@ -266,13 +358,13 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
       const int blk = (a.bs_log2 >= 0) ? (kb >> a.bs_log2) : (kb / a.BS);
       const int phys = ld_uniform(btrow + blk);
       const int valid = min(16, kv1 - kb);
-      boff = ((int64_t)phys * a.BS + (kb - blk * a.BS)) * row_elems * 2 + kv_bytes;
-      nrec = (valid - 1) * (int)(row_elems * 2) + D * 2;
+      boff = ((int64_t)phys * a.BS + (kb - blk * a.BS)) * row_elems * ES + kv_bytes;
+      nrec = (valid - 1) * (int)(row_elems * ES) + D * ES;
     }
     const __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(cache_b + boff), 0, nrec, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(cache_b + a.plane * 2 + boff), 0, nrec, 0x00020000);
+        const_cast<uint8_t*>(cache_b + a.plane * ES + boff), 0, nrec, 0x00020000);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       bf[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, voff[i], 0, 2));
@@ -301,8 +393,18 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         const int row = lr + LPR * i;
-        *reinterpret_cast<u32x4_t*>(wl + row * RB + swz<CPR>(row, lc) * 16) = buf[p][i];
-        *reinterpret_cast<u32x4_t*>(wl + (16 + row) * RB + swz<CPR>(row, lc) * 16) = buf[p][NLD + i];
+        if constexpr (FP8) {
+          u32x4_t k0, k1, v0, v1;
+          e4m3x16_to_bf16(buf[p][i], k0, k1);
+          e4m3x16_to_bf16(buf[p][NLD + i], v0, v1);
+          *reinterpret_cast<u32x4_t*>(wl + row * RB + swz<CPR>(row, 2 * lc) * 16) = k0;
+          *reinterpret_cast<u32x4_t*>(wl + row * RB + swz<CPR>(row, 2 * lc + 1) * 16) = k1;
+          *reinterpret_cast<u32x4_t*>(wl + (16 + row) * RB + swz<CPR>(row, 2 * lc) * 16) = v0;
+          *reinterpret_cast<u32x4_t*>(wl + (16 + row) * RB + swz<CPR>(row, 2 * lc + 1) * 16) = v1;
+        } else {
+          *reinterpret_cast<u32x4_t*>(wl + row * RB + swz<CPR>(row, lc) * 16) = buf[p][i];
+          *reinterpret_cast<u32x4_t*>(wl + (16 + row) * RB + swz<CPR>(row, lc) * 16) = buf[p][NLD + i];
+        }
       }
       issue(buf[p], st + PF);
       const int kb = kv0 + 16 * (wave + 4 * st);
@@ -319,7 +421,7 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = kb + 4 * g + i;
-        x[i] = (key >= kv1 || key > row_limit) ? kNegInf : s[i] * a.scale_log2;
+        x[i] = (key >= kv1 || key > row_limit) ? kNegInf : s[i] * sl2;
       }
       float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       mx = wave_max_xor(mx, 16);
@@ -389,7 +491,7 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
       Lr += wt[w] * sr[w * 16 + er];
     }
     const bool empty = !(L > 0.f);
-    const float inv = empty ? 0.f : 1.f / Lr;
+    const float inv = empty ? 0.f : vsc / Lr;
     const float lse_v = empty ? kNegInf : (M + __log2f(L)) * kLn2;
     float acc[DPT];
 #pragma unroll
@@ -426,10 +528,10 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
   }
 }
 
-template <int D>
+template <int D, bool FP8>
 __global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[small_lds_bytes<D>()];
-  small_body<D>(a, a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS, smem);
+  small_body<D, FP8>(a, a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -462,7 +564,7 @@ constexpr int tiled_lds_bytes() {
   return 2 * 64 * (D + 8) * 2 + 2 * 64 * (D + 32) * 2;
 }
 
-template <int D>
+template <int D, bool FP8>
 __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* item, uint8_t* smem) {
   constexpr int NKT = D / 16;       // QK k-steps (16 d each)
   constexpr int NDT = D / 32;       // 32-wide d tiles of O^T
@@ -496,6 +598,10 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
   const int tok = r / G;
   const int head = it.kvh * G + (r - tok * G);
   const int row_limit = a.causal ? tok + Lk - Lq : INT_MAX;
+  // an E4M3 cache holds K / k_scale and V / v_scale of each KV head: the
+  // scores take k_scale inside the exponent's factor, O takes v_scale at the end
+  const float sl2 = FP8 ? a.scale_log2 * ld_uniform(a.k_scale + it.kvh) : a.scale_log2;
+  const float vsc = FP8 ? ld_uniform(a.v_scale + it.kvh) : 1.f;
   // every row of this wave sees keys up to at least wave_limit
   const int wave_limit = a.causal ? (it.row0 + wave * 32) / G + Lk - Lq : INT_MAX;
 
@@ -566,6 +672,60 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
     }
   };
 
+  // E4M3 cache: this thread moves 16-byte chunk lcol8 (16 elements) of key
+  // rows lkey8 + KSTEP8*i of both planes and widens them to bf16 in LDS.  The
+  // tile's four 16-key groups each lie in one cache block: four scalar
+  // lookups, and each lane takes its group's.
+  constexpr int CPR8 = D / 16;
+  constexpr int LOADS8 = 64 * CPR8 / 256;
+  constexpr int KSTEP8 = 256 / CPR8;
+  static_assert(LOADS8 >= 1, "E4M3 tile loader");
+  const int lkey8 = tid / CPR8, lcol8 = tid % CPR8;
+  const uint8_t* cbase8 = reinterpret_cast<const uint8_t*>(a.cache) + (int64_t)it.kvh * D + lcol8 * 16;
+  u32x4_t k8[FP8 ? LOADS8 : 1], v8[FP8 ? LOADS8 : 1];
+  auto load_tile8 = [&](int j0) {
+    int phys16[4], base16[4];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int kg = min(j0 + 16 * g4, kv1 - 1);
+      const int blk = (bs_log2 >= 0) ? (kg >> bs_log2) : (kg / a.BS);
+      base16[g4] = (j0 + 16 * g4) - blk * a.BS;
+      phys16[g4] = ld_uniform(btrow + blk);
+    }
+#pragma unroll
+    for (int i = 0; i < LOADS8; ++i) {
+      const int kk = KSTEP8 * i + lkey8;
+      const int grp = kk >> 4;
+      int ph = phys16[0], bs = base16[0];
+#pragma unroll
+      for (int g4 = 1; g4 < 4; ++g4) {
+        ph = (grp == g4) ? phys16[g4] : ph;
+        bs = (grp == g4) ? base16[g4] : bs;
+      }
+      if (j0 + kk < kv1) {
+        const uint8_t* p8 = cbase8 + ((int64_t)ph * a.BS + bs + (kk & 15)) * row_elems;
+        k8[i] = *reinterpret_cast<const u32x4_t*>(p8);
+        v8[i] = *reinterpret_cast<const u32x4_t*>(p8 + a.plane);
+      } else {
+        k8[i] = u32x4_t{0u, 0u, 0u, 0u};
+        v8[i] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto store_tile8 = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LOADS8; ++i) {
+      const int kk = KSTEP8 * i + lkey8;
+      u32x4_t lo, hi;
+      e4m3x16_to_bf16(k8[i], lo, hi);
+      *reinterpret_cast<u32x4_t*>(kl[buf] + kk * KP + lcol8 * 16) = lo;
+      *reinterpret_cast<u32x4_t*>(kl[buf] + kk * KP + lcol8 * 16 + 8) = hi;
+      e4m3x16_to_bf16(v8[i], lo, hi);
+      *reinterpret_cast<u32x4_t*>(vl[buf] + kk * VP + lcol8 * 16) = lo;
+      *reinterpret_cast<u32x4_t*>(vl[buf] + kk * VP + lcol8 * 16 + 8) = hi;
+    }
+  };
+
   // l_run sums the fp32 probabilities (for the LSE), lr_run the bf16-rounded
   // ones that the PV product multiplies (for the normalisation of O)
   float m_run = kNegInf, l_run = 0.f, lr_run = 0.f;
@@ -613,7 +773,7 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
     float mx = x[0];
 #pragma unroll
     for (int i = 1; i < 32; ++i) mx = fmaxf(mx, x[i]);
-    mx = wave_max_xor(mx, 32) * a.scale_log2;
+    mx = wave_max_xor(mx, 32) * sl2;
     if (__builtin_expect(__any(mx > m_run + kRescaleSlack), 0)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -627,7 +787,7 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
     float ps[4] = {0.f, 0.f, 0.f, 0.f};     // four independent partial sums
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], a.scale_log2, neg_m));
+      x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], sl2, neg_m));
       ps[i & 3] += x[i];
     }
     l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
@@ -664,23 +824,35 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
   // one barrier per tile: after it, buffer buf holds tile j0 and every wave
   // has finished reading buffer buf^1 (tile j0-64), which the registers of
   // tile j0+64 overwrite once this tile's compute is done
+  auto load_any = [&](int jt) {
+    if constexpr (FP8)
+      load_tile8(jt);
+    else
+      load_tile(jt);
+  };
+  auto store_any = [&](int b) {
+    if constexpr (FP8)
+      store_tile8(b);
+    else
+      store_tile(b);
+  };
   int j0 = it.kv0, buf = 0;
-  if (j0 < kv1) load_tile(j0);
+  if (j0 < kv1) load_any(j0);
   // the first tile's loads and the Q loads are in flight together; all of
   // them must have landed before the loop: otherwise the wait-count pass
   // treats the Q loads as possibly in flight inside the loop and makes
   // every QK MFMA wait for the next tile's prefetch loads as well
   __builtin_amdgcn_s_waitcnt(0);
-  if (j0 < kv1) store_tile(0);
+  if (j0 < kv1) store_any(0);
   __syncthreads();
   for (; j0 < kv1; j0 += 64, buf ^= 1) {
     const bool more = j0 + 64 < kv1;
-    if (more) load_tile(j0 + 64);
+    if (more) load_any(j0 + 64);
     if (j0 + 64 > kv1 || j0 + 63 > wave_limit)
       tile(j0, buf, Bool<true>{});
     else
       tile(j0, buf, Bool<false>{});
-    if (more) store_tile(buf ^ 1);
+    if (more) store_any(buf ^ 1);
     __syncthreads();
   }
 
@@ -688,7 +860,7 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
   lr_run += __shfl_xor(lr_run, 32);
   if (!row_ok) return;
   const bool empty = !(l_run > 0.f);
-  const float inv = empty ? 0.f : 1.f / lr_run;
+  const float inv = empty ? 0.f : vsc / lr_run;
   const float lse_v = empty ? kNegInf : (m_run + __log2f(l_run)) * kLn2;
   // lane (n, h) reg i of tile dt holds O^T[d = 32dt + 8(i/4) + 4h + i%4][row n]
   if (it.prow < 0) {
@@ -717,10 +889,10 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
   }
 }
 
-template <int D>
+template <int D, bool FP8>
 __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_tiled_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[tiled_lds_bytes<D>()];
-  tiled_body<D>(a, a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS, smem);
+  tiled_body<D, FP8>(a, a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -730,15 +902,15 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_tiled_kernel(Att
 // the matrix-core-bound tiled ones share the compute units instead of
 // running one kernel after the other.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool FP8>
 __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_mixed_kernel(AttnArgs a) {
   constexpr int L = small_lds_bytes<D>() > tiled_lds_bytes<D>() ? small_lds_bytes<D>() : tiled_lds_bytes<D>();
   __shared__ __attribute__((aligned(16))) uint8_t smem[L];
   const int32_t* item = a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS;
   if (ld_uniform(item + 7))
-    tiled_body<D>(a, item, smem);
+    tiled_body<D, FP8>(a, item, smem);
   else
-    small_body<D>(a, item, smem);
+    small_body<D, FP8>(a, item, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -866,19 +1038,19 @@ __global__ __launch_bounds__(256) void merge_states_kernel(
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-template <int D>
+template <int D, bool FP8>
 pa_status launch_fwd(const AttnArgs& base, const pa_plan_info* plan, const int32_t* worklist,
                      hipStream_t stream) {
   const int32_t* items = worklist + PA_WORKLIST_HEADER_WORDS;
   AttnArgs a = base;
   a.items = items;
   if (plan->num_small_items > 0 && plan->num_tiled_items > 0) {
-    hipLaunchKernelGGL(attn_mixed_kernel<D>,
+    hipLaunchKernelGGL((attn_mixed_kernel<D, FP8>),
                        dim3(plan->num_small_items + plan->num_tiled_items), dim3(256), 0, stream, a);
   } else if (plan->num_small_items > 0) {
-    hipLaunchKernelGGL(attn_small_kernel<D>, dim3(plan->num_small_items), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_small_kernel<D, FP8>), dim3(plan->num_small_items), dim3(256), 0, stream, a);
   } else if (plan->num_tiled_items > 0) {
-    hipLaunchKernelGGL(attn_tiled_kernel<D>, dim3(plan->num_tiled_items), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_tiled_kernel<D, FP8>), dim3(plan->num_tiled_items), dim3(256), 0, stream, a);
   }
   if (plan->num_reduce_items > 0) {
     const int32_t* r =
@@ -922,11 +1094,48 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, int64_t key_r
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-pa_status pa_varlen_fwd(const pa_attn_params* p, const pa_plan_info* plan, const int32_t* worklist,
-                        const void* q, const void* kv_cache, const int32_t* cu_seqlens_q,
-                        const int32_t* seqused_k, const int32_t* block_table, int32_t num_tokens,
-                        void* out, float* lse, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream) {
+pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, int64_t key_row_stride,
+                                   int64_t value_row_stride, void* kv_cache,
+                                   const int64_t* slot_mapping, const float* k_scale,
+                                   const float* v_scale, int32_t num_tokens, int32_t num_kv_heads,
+                                   int32_t head_size, int32_t num_blocks, int32_t block_size,
+                                   hipStream_t stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_size <= 0 || head_size % 16 != 0 ||
+      head_size > 4096 || num_blocks <= 0 || block_size <= 0 || block_size % 16 != 0)
+    return PA_ERR_INVALID_ARGUMENT;
+  const int64_t row = (int64_t)num_kv_heads * head_size;
+  if (key_row_stride < row || value_row_stride < row || key_row_stride % 8 != 0 ||
+      value_row_stride % 8 != 0)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !kv_cache || !slot_mapping || !k_scale || !v_scale)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(kv_cache, 16) ||
+      !aligned(slot_mapping, 8) || !aligned(k_scale, 4) || !aligned(v_scale, 4))
+    return PA_ERR_INVALID_ARGUMENT;
+  const int64_t plane = (int64_t)num_blocks * block_size * row;   // bytes
+  const int32_t cpr = (int32_t)(row / 16);
+  const int64_t total = (int64_t)num_tokens * 2 * cpr;
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks > INT32_MAX) return PA_ERR_INVALID_ARGUMENT;
+  hipLaunchKernelGGL(reshape_and_cache_fp8_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),
+                     key_row_stride, value_row_stride, static_cast<uint8_t*>(kv_cache),
+                     slot_mapping, k_scale, v_scale, total, cpr, head_size / 16, row, plane);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // extern "C"
+
+namespace {
+
+// pa_varlen_fwd and pa_varlen_fwd_fp8: fp8 selects the E4M3 cache with its
+// per-KV-head scales
+pa_status varlen_fwd(const pa_attn_params* p, const pa_plan_info* plan, const int32_t* worklist,
+                     const void* q, const void* kv_cache, const int32_t* cu_seqlens_q,
+                     const int32_t* seqused_k, const int32_t* block_table, const float* k_scale,
+                     const float* v_scale, bool fp8, int32_t num_tokens, void* out, float* lse,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
   pa_status st = pa::check_params(p);
   if (st != PA_OK) return st;
   if (!plan) return PA_ERR_INVALID_ARGUMENT;
@@ -947,6 +1156,8 @@ pa_status pa_varlen_fwd(const pa_attn_params* p, const pa_plan_info* plan, const
     return PA_ERR_INVALID_ARGUMENT;
   if (n_items == 0) return PA_OK;
   if (!worklist || !q || !kv_cache || !cu_seqlens_q || !seqused_k || !block_table || !out)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
     return PA_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(worklist, 4) ||
       (lse && !aligned(lse, 4)))
@@ -979,12 +1190,40 @@ pa_status pa_varlen_fwd(const pa_attn_params* p, const pa_plan_info* plan, const
   for (int b = 0; b < 31; ++b)
     if ((1 << b) == p->block_size) a.bs_log2 = b;
   a.scale_log2 = p->scale * kLog2e;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   switch (p->head_size) {
-    case 64: return launch_fwd<64>(a, plan, worklist, stream);
-    case 128: return launch_fwd<128>(a, plan, worklist, stream);
-    case 256: return launch_fwd<256>(a, plan, worklist, stream);
+    case 64: return fp8 ? launch_fwd<64, true>(a, plan, worklist, stream)
+                        : launch_fwd<64, false>(a, plan, worklist, stream);
+    case 128: return fp8 ? launch_fwd<128, true>(a, plan, worklist, stream)
+                         : launch_fwd<128, false>(a, plan, worklist, stream);
+    case 256: return fp8 ? launch_fwd<256, true>(a, plan, worklist, stream)
+                         : launch_fwd<256, false>(a, plan, worklist, stream);
   }
   return PA_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_varlen_fwd(const pa_attn_params* p, const pa_plan_info* plan, const int32_t* worklist,
+                        const void* q, const void* kv_cache, const int32_t* cu_seqlens_q,
+                        const int32_t* seqused_k, const int32_t* block_table, int32_t num_tokens,
+                        void* out, float* lse, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  return varlen_fwd(p, plan, worklist, q, kv_cache, cu_seqlens_q, seqused_k, block_table, nullptr,
+                    nullptr, false, num_tokens, out, lse, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_varlen_fwd_fp8(const pa_attn_params* p, const pa_plan_info* plan,
+                            const int32_t* worklist, const void* q, const void* kv_cache,
+                            const int32_t* cu_seqlens_q, const int32_t* seqused_k,
+                            const int32_t* block_table, const float* k_scale, const float* v_scale,
+                            int32_t num_tokens, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  return varlen_fwd(p, plan, worklist, q, kv_cache, cu_seqlens_q, seqused_k, block_table, k_scale,
+                    v_scale, true, num_tokens, out, lse, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_merge_attn_states(void* out, float* out_lse, const void* prefix_out,

@@ -33,7 +33,8 @@ PA_ITEM_WORDS = 8
 PLAN_TARGET_CUS = 256          # compute units the planner schedules for (PA_PLAN_TARGET_CUS)
 
 EXPORTED = ["pa_status_str", "pa_version", "pa_supported_head_sizes", "pa_plan_varlen",
-            "pa_cascade_split", "pa_reshape_and_cache", "pa_varlen_fwd", "pa_merge_attn_states"]
+            "pa_cascade_split", "pa_reshape_and_cache", "pa_varlen_fwd", "pa_merge_attn_states",
+            "pa_reshape_and_cache_fp8", "pa_varlen_fwd_fp8"]
 
 
 class PaError(RuntimeError):
@@ -95,6 +96,14 @@ def lib() -> ctypes.CDLL:
         L.pa_varlen_fwd.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(PlanInfo), _P,
                                     _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P,
                                     ctypes.c_size_t, _P]
+        L.pa_reshape_and_cache_fp8.restype = ctypes.c_int
+        L.pa_reshape_and_cache_fp8.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_int64, _P, _P,
+                                               _P, _P, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P]
+        L.pa_varlen_fwd_fp8.restype = ctypes.c_int
+        L.pa_varlen_fwd_fp8.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(PlanInfo), _P,
+                                        _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P,
+                                        ctypes.c_size_t, _P]
         L.pa_merge_attn_states.restype = ctypes.c_int
         L.pa_merge_attn_states.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int32, _P]
@@ -220,6 +229,43 @@ def pa_varlen_fwd(params: AttnParams, plan: PlanInfo, worklist, q, kv_cache, cu_
     _check(st, "pa_varlen_fwd")
 
 
+def pa_reshape_and_cache_fp8(key, value, kv_cache, slot_mapping, k_scale, v_scale, stream=None):
+    """key/value: bf16 [T, Hkv, D]; kv_cache: uint8 (E4M3) [2, NB, BS, Hkv, D]
+    contiguous; slot_mapping int64 [T]; k_scale/v_scale fp32 [Hkv]."""
+    import torch
+    T, Hkv, D = key.shape
+    if value.shape != key.shape or key.stride(2) != 1 or value.stride(2) != 1 \
+            or key.stride(1) != D or value.stride(1) != D:
+        raise ValueError("key/value must be [T, Hkv, D] with contiguous heads")
+    if not kv_cache.is_contiguous() or kv_cache.dim() != 5 or kv_cache.shape[0] != 2:
+        raise ValueError("kv_cache must be a contiguous (2, NB, BS, Hkv, D) tensor")
+    if slot_mapping.shape[0] != T or k_scale.numel() != Hkv or v_scale.numel() != Hkv:
+        raise ValueError("slot_mapping must have one entry per token, the scales one per KV head")
+    st = lib().pa_reshape_and_cache_fp8(
+        _dev(key, "key", torch.bfloat16), _dev(value, "value", torch.bfloat16),
+        key.stride(0), value.stride(0), _dev(kv_cache, "kv_cache", torch.uint8),
+        _dev(slot_mapping, "slot_mapping", torch.int64), _dev(k_scale, "k_scale", torch.float32),
+        _dev(v_scale, "v_scale", torch.float32), T, Hkv, D, kv_cache.shape[1], kv_cache.shape[2],
+        _stream(stream))
+    _check(st, "pa_reshape_and_cache_fp8")
+
+
+def pa_varlen_fwd_fp8(params: AttnParams, plan: PlanInfo, worklist, q, kv_cache, cu_seqlens_q,
+                      seqused_k, block_table, k_scale, v_scale, out, lse=None, workspace=None,
+                      stream=None):
+    import torch
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().pa_varlen_fwd_fp8(
+        ctypes.byref(params), ctypes.byref(plan), _dev(worklist, "worklist", torch.int32),
+        _dev(q, "q", torch.bfloat16), _dev(kv_cache, "kv_cache", torch.uint8),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(seqused_k, "seqused_k", torch.int32),
+        _dev(block_table, "block_table", torch.int32), _dev(k_scale, "k_scale", torch.float32),
+        _dev(v_scale, "v_scale", torch.float32), int(q.shape[0]),
+        _dev(out, "out", torch.bfloat16), _dev(lse, "lse", torch.float32),
+        _dev(workspace, "workspace"), ws_bytes, _stream(stream))
+    _check(st, "pa_varlen_fwd_fp8")
+
+
 def pa_merge_attn_states(out, out_lse, prefix_out, prefix_lse, suffix_out, suffix_lse,
                          stream=None):
     import torch
@@ -268,14 +314,20 @@ def plan_varlen(q_shape, kv_cache_shape, block_table_shape, host_cu_seqlens_q, h
 
 
 def varlen_fwd(q, kv_cache, cu_seqlens_q, seqused_k, block_table, plan: VarlenPlan,
-               out=None, lse=None, stream=None):
+               out=None, lse=None, stream=None, k_scale=None, v_scale=None):
+    """bf16 cache, or (k_scale and v_scale given) a uint8 E4M3 cache."""
     import torch
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
-    pa_varlen_fwd(plan.params, plan.info, plan.worklist, q, kv_cache, cu_seqlens_q, seqused_k,
-                  block_table, out, lse, plan.workspace, stream)
+    if k_scale is None and v_scale is None:
+        pa_varlen_fwd(plan.params, plan.info, plan.worklist, q, kv_cache, cu_seqlens_q, seqused_k,
+                      block_table, out, lse, plan.workspace, stream)
+    else:
+        pa_varlen_fwd_fp8(plan.params, plan.info, plan.worklist, q, kv_cache, cu_seqlens_q,
+                          seqused_k, block_table, k_scale, v_scale, out, lse, plan.workspace,
+                          stream)
     return out, lse
 
 

@@ -340,6 +340,25 @@ def to_device(wl: Workload, device="cuda") -> dict:
     }
 
 
+def fp8_cache_codes(wl: Workload, seed: int) -> np.ndarray:
+    """A uint8 (E4M3) cache of the workload's shape: every slot that holds a
+    value in the bf16 cache gets a random code of magnitude 0x00..0x57
+    (|value| <= 15) and a random sign; every SENTINEL slot gets the NaN code
+    0x7F, so that a read of a slot outside the keys shows up as NaN."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 0x58, size=wl.kv_cache.shape, dtype=np.uint8)
+    codes |= (rng.integers(0, 2, size=wl.kv_cache.shape, dtype=np.uint8) << 7).astype(np.uint8)
+    codes[wl.kv_cache == SENTINEL] = 0x7F
+    return codes
+
+
+def fp8_scales(num_kv_heads: int, seed: int):
+    """Per-KV-head fp32 (k_scale, v_scale), uniform in [0.02, 0.1]."""
+    rng = np.random.default_rng(seed)
+    return (rng.uniform(0.02, 0.1, num_kv_heads).astype(np.float32),
+            rng.uniform(0.02, 0.1, num_kv_heads).astype(np.float32))
+
+
 def bf16_tensor_bits(t) -> np.ndarray:
     """Device/host bf16 tensor -> numpy uint16 bit patterns."""
     import torch

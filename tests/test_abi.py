@@ -140,6 +140,37 @@ def test_fwd_validation_before_launch(L):
     assert _fwd_call(L, p3, info) == ops.PA_ERR_UNSUPPORTED
 
 
+def test_fp8_entry_points_validate_before_launch(L):
+    P = ctypes.c_void_p
+    E = ops.PA_ERR_INVALID_ARGUMENT
+    p = params()
+    _, info = ops.pa_plan_varlen(p, CU, SK, force_splits=3)
+
+    def fwd8(ks=0x9000, vs=0x9100, **kw):
+        a = dict(worklist=0x1000, q=0x2000, kv=0x3000, cu=0x4000, sk=0x5000, bt=0x6000,
+                 out=0x7000, lse=0x8000, ws=0x10000)
+        a.update(kw)
+        return L.pa_varlen_fwd_fp8(ctypes.byref(p), ctypes.byref(info), P(a["worklist"]), P(a["q"]),
+                                   P(a["kv"]), P(a["cu"]), P(a["sk"]), P(a["bt"]), P(ks), P(vs),
+                                   info.num_tokens, P(a["out"]), P(a["lse"]), P(a["ws"]), 1 << 30, None)
+    assert fwd8(ks=0) == E                       # a scale pointer is required
+    assert fwd8(vs=0) == E
+    assert fwd8(ks=0x9002) == E                  # misaligned scales
+    assert fwd8(q=0) == E
+
+    def rc8(**kw):
+        a = dict(k=0x1000, v=0x2000, ks_=128, vs_=128, c=0x3000, s=0x4000, kscale=0x5000,
+                 vscale=0x6000, T=4, Hkv=2, D=64, NB=4, BS=16)
+        a.update(kw)
+        return L.pa_reshape_and_cache_fp8(P(a["k"]), P(a["v"]), a["ks_"], a["vs_"], P(a["c"]),
+                                          P(a["s"]), P(a["kscale"]), P(a["vscale"]), a["T"],
+                                          a["Hkv"], a["D"], a["NB"], a["BS"], None)
+    assert rc8(D=72, ks_=144, vs_=144) == E       # head size not a multiple of 16
+    assert rc8(kscale=0) == E and rc8(vscale=0) == E
+    assert rc8(BS=24) == E
+    assert rc8(T=0, k=0, v=0, c=0, s=0, kscale=0, vscale=0) == ops.PA_OK   # no launch
+
+
 def test_reshape_and_cache_validation(L):
     P = ctypes.c_void_p
     E = ops.PA_ERR_INVALID_ARGUMENT
