@@ -1,13 +1,17 @@
 """Benchmark of the paged varlen attention path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--secondary]
+                    [--kv-dtype bf16|fp8]
 
 A step is one pass of the whole path over one batch that is already resident
 in HBM: the host planner (pa_plan_varlen, whose work list is copied to the
 device from pinned memory), pa_reshape_and_cache for the batch's new tokens,
 and pa_varlen_fwd (attention kernels + split-KV reduce); the cascade workload
 adds its two passes and pa_merge_attn_states.  The headline workload is the
-64-sequence Llama-3-8B-shaped decode batch.
+64-sequence Llama-3-8B-shaped decode batch.  With --kv-dtype fp8 the cache
+holds E4M3 codes (one byte per element, per-KV-head scales): the cache write
+is pa_reshape_and_cache_fp8, attention pa_varlen_fwd_fp8, and the
+algorithmic KV bytes are one per element.
 
 Printed: one JSON line with the whole-step throughput (algorithmic KV bytes
 per second), a roofline object for the attention call -- its algorithmic
@@ -46,18 +50,28 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary", action="store_true",
                     help="also time the prefill mix and the long-context decode")
+    ap.add_argument("--kv-dtype", choices=("bf16", "fp8"), default="bf16",
+                    help="KV-cache format: bf16, or E4M3 codes with per-KV-head scales")
     return ap.parse_args()
 
 
 class Step:
     """Everything one step needs, resident on the GPU."""
 
-    def __init__(self, wl, dev):
+    def __init__(self, wl, dev, fp8=False):
         import torch
         from paged_kv_varlen_flash_amd import ops, workloads as W
-        self.ops, self.wl = ops, wl
+        self.ops, self.wl, self.fp8 = ops, wl, fp8
         self.d = W.to_device(wl, dev)
         d = self.d
+        if fp8:
+            if wl.spec.shared_prefix:
+                raise SystemExit("--kv-dtype fp8 covers the single-pass workloads")
+            self.codes = W.fp8_cache_codes(wl, 4000)
+            self.k_scale, self.v_scale = W.fp8_scales(wl.Hkv, 4001)
+            d["kv_cache"] = torch.from_numpy(self.codes).to(dev)
+            d["k_scale"] = torch.from_numpy(self.k_scale).to(dev)
+            d["v_scale"] = torch.from_numpy(self.v_scale).to(dev)
         self.params = ops.make_params(wl.B, wl.H, wl.Hkv, wl.D, wl.BS, wl.num_blocks,
                                       wl.block_table.shape[1], wl.causal, wl.scale)
         self.cu = np.ascontiguousarray(wl.cu_seqlens_q, np.int32)
@@ -109,11 +123,19 @@ class Step:
 
     def scatter(self):
         d = self.d
-        self.ops.pa_reshape_and_cache(d["key"], d["value"], d["kv_cache"], d["slot_mapping"])
+        if self.fp8:
+            self.ops.pa_reshape_and_cache_fp8(d["key"], d["value"], d["kv_cache"],
+                                              d["slot_mapping"], d["k_scale"], d["v_scale"])
+        else:
+            self.ops.pa_reshape_and_cache(d["key"], d["value"], d["kv_cache"], d["slot_mapping"])
 
     def attention(self):
         d, ops = self.d, self.ops
-        if self.cascade is None:
+        if self.fp8:
+            ops.pa_varlen_fwd_fp8(self.params, self.info, self.worklist, d["q"], d["kv_cache"],
+                                  d["cu_seqlens_q"], d["seqused_k"], d["block_table"],
+                                  d["k_scale"], d["v_scale"], self.out, self.lse, self.workspace)
+        elif self.cascade is None:
             ops.pa_varlen_fwd(self.params, self.info, self.worklist, d["q"], d["kv_cache"],
                               d["cu_seqlens_q"], d["seqused_k"], d["block_table"], self.out,
                               self.lse, self.workspace)
@@ -197,11 +219,20 @@ def blas_threads():
         return 1
 
 
-def cpu_baseline(wl, budget_s):
+def cpu_baseline(wl, budget_s, fp8_step=None):
     """The fp64 oracle (as it stands) on whole sequences of the same batch
     until the time budget is used; KV-read GB/s over the sequences done."""
     import oracle.attention as OA
-    cache = OA.reshape_and_cache(wl.key, wl.value, wl.kv_cache, wl.slot_mapping)
+    scales = {}
+    es = 2
+    if fp8_step is None:
+        cache = OA.reshape_and_cache(wl.key, wl.value, wl.kv_cache, wl.slot_mapping)
+    else:
+        import oracle.fp8 as OF8
+        ks, vs = fp8_step.k_scale, fp8_step.v_scale
+        cache = OF8.reshape_and_cache_fp8(wl.key, wl.value, fp8_step.codes, wl.slot_mapping, ks, vs)
+        scales = {"k_scale": ks, "v_scale": vs}
+        es = 1
     done, nbytes = 0, 0
     t0 = time.perf_counter()
     # whole sequences, cycling through the batch, until the budget is spent
@@ -209,8 +240,8 @@ def cpu_baseline(wl, budget_s):
         b = done % wl.B
         t_a, t_b = int(wl.cu_seqlens_q[b]), int(wl.cu_seqlens_q[b + 1])
         OA.varlen_attention(wl.q[t_a:t_b], cache, np.array([0, t_b - t_a]), wl.k_lens[b:b + 1],
-                            wl.block_table[b:b + 1], wl.scale, wl.causal)
-        nbytes += 2 * int(wl.k_lens[b]) * wl.Hkv * wl.D * 2
+                            wl.block_table[b:b + 1], wl.scale, wl.causal, **scales)
+        nbytes += 2 * int(wl.k_lens[b]) * wl.Hkv * wl.D * es
         done += 1
     el = time.perf_counter() - t0
     return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": blas_threads(),
@@ -219,19 +250,19 @@ def cpu_baseline(wl, budget_s):
                       f"({nbytes/1e6:.1f} MB of KV), fp64 numpy, {el:.1f} s wall"}
 
 
-def measure(name, args, dev, flush, with_cpu):
+def measure(name, args, dev, flush, with_cpu, fp8=False):
     import torch
     from paged_kv_varlen_flash_amd import workloads as W
     wl = W.make(name)
-    step = Step(wl, dev)
+    step = Step(wl, dev, fp8)
     per_step = time_steps(step, args.steps, args.warmup)
     t_mean, t_med = time_attention(step, args.kernel_reps, flush)
-    kv = wl.kv_read_bytes()
+    kv = wl.kv_read_bytes() // (2 if fp8 else 1)
     flops = wl.attention_flops()
     res = {"workload": name, "wl": wl, "ms_per_step": per_step * 1e3, "attn_mean_s": t_mean,
            "attn_median_s": t_med, "kv_bytes": kv, "flops": flops, "plan": step.info.as_dict()}
     if with_cpu:
-        res["cpu"] = cpu_baseline(wl, args.cpu_seconds)
+        res["cpu"] = cpu_baseline(wl, args.cpu_seconds, step if fp8 else None)
     del step
     torch.cuda.empty_cache()
     return res
@@ -259,20 +290,23 @@ def main():
     torch.cuda.synchronize()
     del calib_src, calib_dst
 
-    head = measure(args.workload, args, dev, flush, not args.no_cpu_baseline)
+    fp8 = args.kv_dtype == "fp8"
+    head = measure(args.workload, args, dev, flush, not args.no_cpu_baseline, fp8)
     wl = head["wl"]
+    tkey = args.workload + ("_fp8" if fp8 else "")
+    tname = ", fp8" if fp8 else ""
     decode_like = wl.q_lens.max() * (wl.H // wl.Hkv) <= 16 or args.workload == "cascade_prefix"
     value = head["kv_bytes"] / (head["ms_per_step"] * 1e-3) / 1e9
     if decode_like:
         ach = head["kv_bytes"] / head["attn_mean_s"] / 1e9
-        tr = recorded_traffic(args.workload)
+        tr = recorded_traffic(tkey)
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4),
                 "traffic": (tr["read_bytes"] + tr["write_bytes"]) if tr else None,
                 "traffic_read_over_algorithmic": (round(tr["read_bytes"] / head["kv_bytes"], 4)
                                                   if tr else None),
-                "kernel": "pa_varlen_fwd (attn_small_kernel<%d> + split_reduce_kernel<%d>)"
-                          % (wl.D, wl.D),
+                "kernel": "pa_varlen_fwd%s (attn_small_kernel<%d%s> + split_reduce_kernel<%d>)"
+                          % ("_fp8" if fp8 else "", wl.D, tname, wl.D),
                 "per_launch_bytes": head["kv_bytes"],
                 "avg_launch_us": round(head["attn_mean_s"] * 1e6, 2),
                 "median_launch_us": round(head["attn_median_s"] * 1e6, 2)}
@@ -287,8 +321,12 @@ def main():
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16, shuffled physical blocks)",
-        "config": dict(wl.summary(), parallelism="none (1 GPU)"),
+        "data": ("synthetic (seeded random E4M3 cache codes, |code value| <= 15, per-KV-head "
+                 "scales in [0.02, 0.1]; new tokens N(0,1) bf16 quantised by the cache write; "
+                 "shuffled physical blocks)" if fp8 else
+                 "synthetic (seeded N(0,1) bf16, shuffled physical blocks)"),
+        "config": dict(wl.summary(), parallelism="none (1 GPU)",
+                       kv_cache_dtype="fp8_e4m3 (per-KV-head scales)" if fp8 else "bf16"),
         "roofline": roof,
     }
     if "cpu" in head:
@@ -306,6 +344,13 @@ def main():
                 ent["attn_TFLOPs"] = round(r["flops"] / r["attn_mean_s"] / 1e12, 1)
                 ent["mfma_frac"] = round(r["flops"] / r["attn_mean_s"] / 1e12 / BF16_PEAK_TFLOPS, 4)
             sec[name] = ent
+        if not fp8:
+            r = measure("decode_llama8b", args, dev, flush, False, fp8=True)
+            sec["decode_llama8b_fp8"] = {
+                "ms_per_step": round(r["ms_per_step"], 4),
+                "attn_avg_us": round(r["attn_mean_s"] * 1e6, 2),
+                "kv_GBps": round(r["kv_bytes"] / r["attn_mean_s"] / 1e9, 1),
+                "hbm_frac": round(r["kv_bytes"] / r["attn_mean_s"] / 1e9 / HBM_PEAK_GBS, 4)}
         line["secondary"] = sec
     print(json.dumps(line), flush=True)
 
