@@ -58,7 +58,7 @@ def parse():
 class Step:
     """Everything one step needs, resident on the GPU."""
 
-    def __init__(self, wl, dev, fp8=False):
+    def __init__(self, wl, dev, fp8=False, single_pass=False):
         import torch
         from paged_kv_varlen_flash_amd import ops, workloads as W
         self.ops, self.wl, self.fp8 = ops, wl, fp8
@@ -92,7 +92,7 @@ class Step:
         self.lse = torch.empty(wl.T, wl.H, dtype=torch.float32, device=dev)
         self.i = 0
         self.cascade = None
-        if wl.spec.shared_prefix:
+        if wl.spec.shared_prefix and not single_pass:
             self.cascade = ops.CascadePlan(tuple(d["q"].shape), tuple(d["kv_cache"].shape),
                                            tuple(d["block_table"].shape), wl.cu_seqlens_q,
                                            wl.k_lens, wl.scale, wl.spec.shared_prefix)
@@ -250,11 +250,11 @@ def cpu_baseline(wl, budget_s, fp8_step=None):
                       f"({nbytes/1e6:.1f} MB of KV), fp64 numpy, {el:.1f} s wall"}
 
 
-def measure(name, args, dev, flush, with_cpu, fp8=False):
+def measure(name, args, dev, flush, with_cpu, fp8=False, single_pass=False):
     import torch
     from paged_kv_varlen_flash_amd import workloads as W
     wl = W.make(name)
-    step = Step(wl, dev, fp8)
+    step = Step(wl, dev, fp8, single_pass)
     per_step = time_steps(step, args.steps, args.warmup)
     t_mean, t_med = time_attention(step, args.kernel_reps, flush)
     kv = wl.kv_read_bytes() // (2 if fp8 else 1)
@@ -340,6 +340,16 @@ def main():
                    "attn_avg_us": round(r["attn_mean_s"] * 1e6, 2),
                    "kv_GBps": round(r["kv_bytes"] / r["attn_mean_s"] / 1e9, 1),
                    "hbm_frac": round(r["kv_bytes"] / r["attn_mean_s"] / 1e9 / HBM_PEAK_GBS, 4)}
+            if name == "cascade_prefix":
+                # the host decision against both measured paths
+                from paged_kv_varlen_flash_amd import ops
+                P, use = ops.pa_cascade_decide(
+                    ops.make_params(w.B, w.H, w.Hkv, w.D, w.BS, w.num_blocks,
+                                    w.block_table.shape[1], w.causal, w.scale),
+                    w.cu_seqlens_q, w.k_lens, w.block_table)
+                one = measure(name, args, dev, flush, False, single_pass=True)
+                ent["single_pass_attn_avg_us"] = round(one["attn_mean_s"] * 1e6, 2)
+                ent["cascade_decision"] = {"common_prefix_len": P, "use_cascade": use}
             if name == "chunked_prefill_mix":
                 ent["attn_TFLOPs"] = round(r["flops"] / r["attn_mean_s"] / 1e12, 1)
                 ent["mfma_frac"] = round(r["flops"] / r["attn_mean_s"] / 1e12 / BF16_PEAK_TFLOPS, 4)

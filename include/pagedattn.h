@@ -152,6 +152,41 @@ pa_status pa_cascade_split(const pa_attn_params* p, int32_t common_prefix_len,
                            int32_t* suffix_seqused_k, int32_t* block_table_col0);
 
 /* ------------------------------------------------------------------------
+ * pa_cascade_decide -- the host cascade decision ("FlashAttention 在 vLLM 中
+ * 的实现分析", section 6.2, use_cascade_attention; section 6.1, a prefix shared
+ * by every request).  Host only; reads nothing on the device.
+ *
+ *   p                  the full (single-pass) problem
+ *   host_cu_seqlens_q, host_seqused_k   host mirrors [B+1], [B]
+ *   host_block_table   host int32 [B, stride] (stride = p->block_table_stride,
+ *                      or p->max_blocks_per_seq when that is 0)
+ *   kv_bytes_per_elem  2 for the bf16 cache, 1 for the E4M3 cache
+ * Outputs:
+ *   common_prefix_len  block_size x the number of leading block-table
+ *                      columns whose entry is the same physical block in
+ *                      every row, cut to what every query token comes after
+ *                      (<= seqused_k[b] - Lq_b, rounded down to whole
+ *                      blocks); 0 when B < 2 or nothing is shared
+ *   use_cascade        1 when the cascade path (pa_cascade_split + two
+ *                      passes + pa_merge_attn_states) should be taken:
+ *                      causal, common_prefix_len >= 256, B >= 8 (the
+ *                      section's thresholds; ALiBi, sliding windows and DCP
+ *                      do not exist here), and the cost model below expects
+ *                      it to be faster than the single pass; else 0.
+ * Cost model (this library's stand-in for the section's comparison of the
+ * two paths' CTA counts, calibrated on MI355X measurements): a pass costs
+ * max(KV bytes / 5.5 TB/s, QK+PV flops of its tiled rows / 0.5 PFLOP/s)
+ * plus 6 us per launch (attention, split reduce, merge); the single pass
+ * reads every sequence's keys, the cascade reads the prefix once, each
+ * suffix, and merges 3 * num_tokens * H * D bf16 values.
+ * Errors: PA_ERR_INVALID_ARGUMENT (bad params or lengths, NULL pointers).
+ * ------------------------------------------------------------------------ */
+pa_status pa_cascade_decide(const pa_attn_params* p, const int32_t* host_cu_seqlens_q,
+                            const int32_t* host_seqused_k, const int32_t* host_block_table,
+                            int32_t kv_bytes_per_elem, int32_t* common_prefix_len,
+                            int32_t* use_cascade);
+
+/* ------------------------------------------------------------------------
  * pa_reshape_and_cache -- scatter the new tokens' keys and values into the
  * paged cache ("FlashAttention 在 vLLM 中的实现分析", section 4.2, the
  * do_kv_cache_update step, and the helper-kernel table of section 8.2).

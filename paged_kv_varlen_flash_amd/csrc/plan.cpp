@@ -6,6 +6,7 @@
 // which key range, and where split-KV partials go.  Pure host code: no HIP
 // call is made here, so every check can run on a machine without a GPU.
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -312,6 +313,70 @@ pa_status pa_plan_varlen(const pa_attn_params* p, const int32_t* host_cu_seqlens
                          pa_plan_info* info) {
   return pa::plan(p, host_cu_seqlens_q, host_seqused_k, force_splits, host_worklist,
                   worklist_capacity_bytes, info);
+}
+
+pa_status pa_cascade_decide(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
+                            const int32_t* bt, int32_t kv_bytes_per_elem,
+                            int32_t* common_prefix_len, int32_t* use_cascade) {
+  pa_status st = pa::check_params(p);
+  if (st != PA_OK) return st;
+  if (!common_prefix_len || !use_cascade) return PA_ERR_INVALID_ARGUMENT;
+  if (kv_bytes_per_elem != 1 && kv_bytes_per_elem != 2) return PA_ERR_INVALID_ARGUMENT;
+  *common_prefix_len = 0;
+  *use_cascade = 0;
+  const int32_t B = p->batch;
+  if (B > 0 && (!cu || !sk || !bt)) return PA_ERR_INVALID_ARGUMENT;
+  if (B > 0 && cu[0] != 0) return PA_ERR_INVALID_ARGUMENT;
+  const int32_t BS = p->block_size;
+  const int32_t stride = p->block_table_stride ? p->block_table_stride : p->max_blocks_per_seq;
+  // the prefix may cover only keys that every query token comes after
+  int64_t limit = INT64_MAX;
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t Lq = cu[b + 1] - cu[b];
+    if (Lq < 0 || sk[b] < 0 || sk[b] > (int64_t)p->max_blocks_per_seq * BS)
+      return PA_ERR_INVALID_ARGUMENT;
+    limit = std::min<int64_t>(limit, (int64_t)sk[b] - Lq);
+  }
+  if (B < 2 || limit < BS) return PA_OK;
+  const int64_t max_blocks = limit / BS;
+  int64_t nblk = 0;
+  for (; nblk < max_blocks; ++nblk) {
+    const int32_t phys = bt[nblk];
+    bool same = phys >= 0 && phys < p->num_blocks;
+    for (int32_t b = 1; same && b < B; ++b) same = bt[(int64_t)b * stride + nblk] == phys;
+    if (!same) break;
+  }
+  const int64_t P = nblk * BS;
+  *common_prefix_len = (int32_t)P;
+  if (!p->causal || P < 256 || B < 8) return PA_OK;
+
+  // cost model: seconds of each path
+  const double bw = 5.5e12, fl = 0.5e15, launch = 6e-6;
+  const int32_t G = p->num_heads / p->num_kv_heads;
+  const double row_bytes = 2.0 * p->num_kv_heads * p->head_size * kv_bytes_per_elem;
+  const int64_t T = cu[B];
+  auto pass_time = [&](double kv_bytes, double tiled_flops, int launches) {
+    return std::max(kv_bytes / bw, tiled_flops / fl) + launches * launch;
+  };
+  double keys_all = 0, keys_suffix = 0, flops_single = 0, flops_suffix = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t Lq = cu[b + 1] - cu[b];
+    keys_all += sk[b];
+    keys_suffix += (double)sk[b] - (double)P;
+    if ((int64_t)Lq * G > PA_SMALL_MAX_ROWS) {   // rows on the tiled kernel
+      flops_single += 4.0 * p->head_size * p->num_heads * (double)Lq * sk[b];
+      flops_suffix += 4.0 * p->head_size * p->num_heads * (double)Lq * ((double)sk[b] - P);
+    }
+  }
+  const double prefix_flops =
+      (T * G > PA_SMALL_MAX_ROWS) ? 4.0 * p->head_size * p->num_heads * (double)T * P : 0.0;
+  const double merge_bytes = 3.0 * T * p->num_heads * p->head_size * 2.0;
+  const double t_single = pass_time(keys_all * row_bytes, flops_single, 2);
+  const double t_cascade = pass_time((double)P * row_bytes, prefix_flops, 2) +
+                           pass_time(keys_suffix * row_bytes, flops_suffix, 2) +
+                           merge_bytes / bw + launch;
+  *use_cascade = t_cascade < t_single ? 1 : 0;
+  return PA_OK;
 }
 
 pa_status pa_cascade_split(const pa_attn_params* p, int32_t common_prefix_len,

@@ -34,7 +34,7 @@ PLAN_TARGET_CUS = 256          # compute units the planner schedules for (PA_PLA
 
 EXPORTED = ["pa_status_str", "pa_version", "pa_supported_head_sizes", "pa_plan_varlen",
             "pa_cascade_split", "pa_reshape_and_cache", "pa_varlen_fwd", "pa_merge_attn_states",
-            "pa_reshape_and_cache_fp8", "pa_varlen_fwd_fp8"]
+            "pa_reshape_and_cache_fp8", "pa_varlen_fwd_fp8", "pa_cascade_decide"]
 
 
 class PaError(RuntimeError):
@@ -88,6 +88,9 @@ def lib() -> ctypes.CDLL:
         L.pa_cascade_split.argtypes = [ctypes.POINTER(AttnParams), ctypes.c_int32, _I32P, _I32P,
                                        ctypes.POINTER(AttnParams), ctypes.POINTER(AttnParams),
                                        _I32P, _I32P, _I32P, _I32P]
+        L.pa_cascade_decide.restype = ctypes.c_int
+        L.pa_cascade_decide.argtypes = [ctypes.POINTER(AttnParams), _I32P, _I32P, _I32P,
+                                        ctypes.c_int32, _I32P, _I32P]
         L.pa_reshape_and_cache.restype = ctypes.c_int
         L.pa_reshape_and_cache.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_int64, _P, _P,
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -175,6 +178,20 @@ def pa_cascade_split(params: AttnParams, common_prefix_len: int, host_cu_seqlens
                                 _ptr_i32(psk), _ptr_i32(ssk), _ptr_i32(col0))
     _check(st, "pa_cascade_split")
     return pp, sp, pcu, psk, ssk[:len(sk)], int(col0[0])
+
+
+def pa_cascade_decide(params: AttnParams, host_cu_seqlens_q, host_seqused_k, host_block_table,
+                      kv_bytes_per_elem: int = 2) -> Tuple[int, bool]:
+    """Host-only cascade decision: (common_prefix_len, use_cascade)."""
+    cu = _i32(host_cu_seqlens_q)
+    sk = _i32(host_seqused_k)
+    bt = _i32(host_block_table)
+    P = np.zeros(1, np.int32)
+    use = np.zeros(1, np.int32)
+    st = lib().pa_cascade_decide(ctypes.byref(params), _ptr_i32(cu), _ptr_i32(sk), _ptr_i32(bt),
+                                 int(kv_bytes_per_elem), _ptr_i32(P), _ptr_i32(use))
+    _check(st, "pa_cascade_decide")
+    return int(P[0]), bool(use[0])
 
 
 def _stream(stream):

@@ -331,3 +331,84 @@ def test_small_items_longest_first(L):
     for seq, kvh, row0, nrows, k0, k1, prow, _ in small:
         if prow >= 0 and k1 != wl.k_lens[seq]:
             assert (k1 - k0) % 64 == 0 and k0 % 64 == 0
+
+
+# ---------------------------------------------------------------- cascade decision
+def _brute_common_prefix(cu, sk, bt, BS, NB):
+    B = len(sk)
+    if B < 2:
+        return 0
+    limit = min(int(sk[b]) - int(cu[b + 1] - cu[b]) for b in range(B))
+    n = 0
+    while (n + 1) * BS <= limit:
+        col = [int(bt[b][n]) for b in range(B)]
+        if col[0] < 0 or col[0] >= NB or any(c != col[0] for c in col):
+            break
+        n += 1
+    return n * BS
+
+
+def test_cascade_decide_on_workloads(L):
+    wl = W.make("cascade_prefix", materialise=False)
+    p = ops.make_params(wl.B, wl.H, wl.Hkv, wl.D, wl.BS, wl.num_blocks, wl.block_table.shape[1],
+                        True, wl.scale)
+    P, use = ops.pa_cascade_decide(p, wl.cu_seqlens_q, wl.k_lens, wl.block_table)
+    assert P == wl.spec.shared_prefix and use
+    P8, use8 = ops.pa_cascade_decide(p, wl.cu_seqlens_q, wl.k_lens, wl.block_table, 1)
+    assert P8 == P and use8
+    wl2 = W.make("decode_llama8b", materialise=False)
+    p2 = ops.make_params(wl2.B, wl2.H, wl2.Hkv, wl2.D, wl2.BS, wl2.num_blocks,
+                         wl2.block_table.shape[1], True, wl2.scale)
+    assert ops.pa_cascade_decide(p2, wl2.cu_seqlens_q, wl2.k_lens, wl2.block_table) == (0, False)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_cascade_common_prefix_brute_force(L, seed):
+    rng = np.random.default_rng(300 + seed)
+    B = int(rng.integers(1, 12))
+    BS = int(rng.choice([16, 32]))
+    shared = int(rng.integers(0, 20))
+    q_lens = rng.integers(1, 40, B)
+    k_lens = q_lens + rng.integers(0, 30 * BS, B)
+    nblk = (k_lens + BS - 1) // BS
+    MB = int(nblk.max()) + 2
+    NB = shared + int(nblk.sum()) + 5
+    bt = np.full((B, MB), -1, np.int32)
+    prefix = rng.permutation(NB)[:shared]
+    free = [x for x in rng.permutation(NB) if x not in set(prefix.tolist())]
+    c = 0
+    for b in range(B):
+        for j in range(int(nblk[b])):
+            if j < shared:
+                bt[b, j] = prefix[j]
+            else:
+                bt[b, j] = free[c]
+                c += 1
+    if B > 1 and shared > 3 and seed % 3 == 0:
+        bt[B - 1, shared - 2] = free[c]          # a row that diverges early
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    p = ops.make_params(B, 8, 2, 64, BS, NB, MB, True, 0.125)
+    P, use = ops.pa_cascade_decide(p, cu, k_lens.astype(np.int32), bt)
+    assert P == _brute_common_prefix(cu, k_lens, bt, BS, NB)
+    assert (not use) or (P >= 256 and B >= 8)
+
+
+def test_cascade_decide_thresholds(L):
+    """The section's thresholds: prefix >= 256 tokens, >= 8 requests, causal;
+    and the cost model declines a prefix that saves little against long
+    private suffixes."""
+    def case(B, P, suffix, causal=True, BS=16):
+        nb_p, nb_s = P // BS, (suffix + BS - 1) // BS
+        bt = np.zeros((B, nb_p + nb_s), np.int32)
+        bt[:, :nb_p] = np.arange(nb_p)
+        bt[:, nb_p:] = nb_p + np.arange(B * nb_s).reshape(B, nb_s)
+        q_lens = np.ones(B, np.int32)
+        k_lens = np.full(B, P + suffix, np.int32)
+        cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+        p = ops.make_params(B, 32, 8, 128, BS, nb_p + B * nb_s, nb_p + nb_s, causal, 0.088)
+        return ops.pa_cascade_decide(p, cu, k_lens, bt)
+    assert case(32, 2048, 300) == (2048, True)
+    assert case(4, 2048, 300) == (2048, False)          # fewer than 8 requests
+    assert case(32, 128, 300) == (128, False)           # prefix below 256
+    assert case(32, 2048, 300, causal=False) == (2048, False)
+    assert case(8, 256, 100000)[1] is False             # saves 0.2 % of the bytes
