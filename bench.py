@@ -250,10 +250,16 @@ def cpu_baseline(wl, budget_s, fp8_step=None):
                       f"({nbytes/1e6:.1f} MB of KV), fp64 numpy, {el:.1f} s wall"}
 
 
+_WORKLOADS = {}
+
+
 def measure(name, args, dev, flush, with_cpu, fp8=False, single_pass=False):
     import torch
     from paged_kv_varlen_flash_amd import workloads as W
-    wl = W.make(name)
+    if name not in _WORKLOADS:
+        print(f"bench: building workload {name}", file=sys.stderr, flush=True)
+        _WORKLOADS[name] = W.make(name)
+    wl = _WORKLOADS[name]
     step = Step(wl, dev, fp8, single_pass)
     per_step = time_steps(step, args.steps, args.warmup)
     t_mean, t_med = time_attention(step, args.kernel_reps, flush)
@@ -350,6 +356,23 @@ def main():
                 one = measure(name, args, dev, flush, False, single_pass=True)
                 ent["single_pass_attn_avg_us"] = round(one["attn_mean_s"] * 1e6, 2)
                 ent["cascade_decision"] = {"common_prefix_len": P, "use_cascade": use}
+        if not fp8:
+            # the decision on a longer shared prefix (64 requests x 16384 shared
+            # tokens): both paths measured next to it
+            from paged_kv_varlen_flash_amd import ops, workloads as W
+            spec = W.Spec(name="cascade_prefix_16k", num_heads=32, num_kv_heads=8, head_size=128,
+                          block_size=16, causal=True, seed=1006, groups=(("decode", 64, 64, 512),),
+                          shared_prefix=16384)
+            W.SPECS[spec.name] = spec
+            w = W.make(spec.name, materialise=False)
+            P, use = ops.pa_cascade_decide(
+                ops.make_params(w.B, w.H, w.Hkv, w.D, w.BS, w.num_blocks, w.block_table.shape[1],
+                                w.causal, w.scale), w.cu_seqlens_q, w.k_lens, w.block_table)
+            casc = measure(spec.name, args, dev, flush, False)
+            one = measure(spec.name, args, dev, flush, False, single_pass=True)
+            sec[spec.name] = {"attn_avg_us": round(casc["attn_mean_s"] * 1e6, 2),
+                              "single_pass_attn_avg_us": round(one["attn_mean_s"] * 1e6, 2),
+                              "cascade_decision": {"common_prefix_len": P, "use_cascade": use}}
             if name == "chunked_prefill_mix":
                 ent["attn_TFLOPs"] = round(r["flops"] / r["attn_mean_s"] / 1e12, 1)
                 ent["mfma_frac"] = round(r["flops"] / r["attn_mean_s"] / 1e12 / BF16_PEAK_TFLOPS, 4)

@@ -350,32 +350,61 @@ pa_status pa_cascade_decide(const pa_attn_params* p, const int32_t* cu, const in
   *common_prefix_len = (int32_t)P;
   if (!p->causal || P < 256 || B < 8) return PA_OK;
 
-  // cost model: seconds of each path
-  const double bw = 5.5e12, fl = 0.5e15, launch = 6e-6;
-  const int32_t G = p->num_heads / p->num_kv_heads;
-  const double row_bytes = 2.0 * p->num_kv_heads * p->head_size * kv_bytes_per_elem;
-  const int64_t T = cu[B];
-  auto pass_time = [&](double kv_bytes, double tiled_flops, int launches) {
-    return std::max(kv_bytes / bw, tiled_flops / fl) + launches * launch;
-  };
-  double keys_all = 0, keys_suffix = 0, flops_single = 0, flops_suffix = 0;
-  for (int32_t b = 0; b < B; ++b) {
-    const int32_t Lq = cu[b + 1] - cu[b];
-    keys_all += sk[b];
-    keys_suffix += (double)sk[b] - (double)P;
-    if ((int64_t)Lq * G > PA_SMALL_MAX_ROWS) {   // rows on the tiled kernel
-      flops_single += 4.0 * p->head_size * p->num_heads * (double)Lq * sk[b];
-      flops_suffix += 4.0 * p->head_size * p->num_heads * (double)Lq * ((double)sk[b] - P);
+  // cost model: plan both paths and price their launches with times fitted
+  // to MI355X measurements of this library (microseconds)
+  const double row_bytes = 2.0 * p->head_size * kv_bytes_per_elem;   // K+V of one key, one KV head
+  const double kv_heads = p->num_kv_heads;
+  // the single pass reads the shared blocks once per sequence; all but the
+  // first read come from the last-level cache while the prefix fits in it
+  const double prefix_bytes = (double)P * row_bytes * kv_heads;
+  const double reread_bw = prefix_bytes <= 128e6 ? 13.6e6 : 6.5e6;   // bytes per us
+  double t_single = 0, t_prefix = 0, t_suffix = 0;
+  std::vector<int32_t> scu(2), ssk(B), pcu(2), psk(1);
+  pa_attn_params pp, sp;
+  int32_t col0 = 0;
+  st = pa_cascade_split(p, (int32_t)P, cu, sk, &pp, &sp, pcu.data(), psk.data(), ssk.data(), &col0);
+  if (st != PA_OK) return st;
+  double t_pass[3];
+  const pa_attn_params* ps[3] = {p, &pp, &sp};
+  const int32_t* cus[3] = {cu, pcu.data(), cu};
+  const int32_t* sks[3] = {sk, psk.data(), ssk.data()};
+  for (int k = 0; k < 3; ++k) {
+    pa_plan_info info;
+    st = pa_plan_varlen(ps[k], cus[k], sks[k], 0, nullptr, 0, &info);
+    if (st != PA_OK) return st;
+    std::vector<int32_t> wl(info.worklist_bytes / 4);
+    st = pa_plan_varlen(ps[k], cus[k], sks[k], 0, wl.data(), info.worklist_bytes, &info);
+    if (st != PA_OK) return st;
+    const int32_t* it = wl.data() + PA_WORKLIST_HEADER_WORDS;
+    double small_keys = 0;
+    int64_t max_tiled_keys = 0;
+    for (int32_t i = 0; i < info.num_small_items + info.num_tiled_items; ++i, it += PA_ITEM_WORDS) {
+      const int64_t keys = std::max(0, it[5] - it[4]);
+      if (it[7] == 0) small_keys += (double)keys;
+      else max_tiled_keys = std::max(max_tiled_keys, keys);
     }
+    double t = 0;
+    if (info.num_small_items > 0) {
+      double bytes = small_keys * row_bytes;
+      if (k == 0) {
+        // the repeated reads of the shared blocks
+        const double reread = (double)(B - 1) * P * kv_heads * row_bytes;
+        bytes -= reread;
+        t += reread / reread_bw;
+      }
+      t += 7.8 + bytes / 6.5e6;
+    }
+    if (info.num_tiled_items > 0)
+      t += 10.8 + 1.15 * (double)((max_tiled_keys + 63) / 64) *
+                      (double)((info.num_tiled_items + 511) / 512);
+    if (info.num_reduce_items > 0) t += 4.2;
+    t_pass[k] = t;
   }
-  const double prefix_flops =
-      (T * G > PA_SMALL_MAX_ROWS) ? 4.0 * p->head_size * p->num_heads * (double)T * P : 0.0;
-  const double merge_bytes = 3.0 * T * p->num_heads * p->head_size * 2.0;
-  const double t_single = pass_time(keys_all * row_bytes, flops_single, 2);
-  const double t_cascade = pass_time((double)P * row_bytes, prefix_flops, 2) +
-                           pass_time(keys_suffix * row_bytes, flops_suffix, 2) +
-                           merge_bytes / bw + launch;
-  *use_cascade = t_cascade < t_single ? 1 : 0;
+  t_single = t_pass[0];
+  t_prefix = t_pass[1];
+  t_suffix = t_pass[2];
+  const double t_merge = 3.4;
+  *use_cascade = (t_prefix + t_suffix + t_merge < t_single) ? 1 : 0;
   return PA_OK;
 }
 

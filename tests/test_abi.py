@@ -352,10 +352,13 @@ def test_cascade_decide_on_workloads(L):
     wl = W.make("cascade_prefix", materialise=False)
     p = ops.make_params(wl.B, wl.H, wl.Hkv, wl.D, wl.BS, wl.num_blocks, wl.block_table.shape[1],
                         True, wl.scale)
+    # measured on MI355X: single pass 37.9 us, cascade 41.4 us (the 8.4 MB
+    # prefix is re-read from the last-level cache): the model keeps the
+    # single pass
     P, use = ops.pa_cascade_decide(p, wl.cu_seqlens_q, wl.k_lens, wl.block_table)
-    assert P == wl.spec.shared_prefix and use
+    assert P == wl.spec.shared_prefix and not use
     P8, use8 = ops.pa_cascade_decide(p, wl.cu_seqlens_q, wl.k_lens, wl.block_table, 1)
-    assert P8 == P and use8
+    assert P8 == P and not use8
     wl2 = W.make("decode_llama8b", materialise=False)
     p2 = ops.make_params(wl2.B, wl2.H, wl2.Hkv, wl2.D, wl2.BS, wl2.num_blocks,
                          wl2.block_table.shape[1], True, wl2.scale)
@@ -407,8 +410,9 @@ def test_cascade_decide_thresholds(L):
         cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
         p = ops.make_params(B, 32, 8, 128, BS, nb_p + B * nb_s, nb_p + nb_s, causal, 0.088)
         return ops.pa_cascade_decide(p, cu, k_lens, bt)
-    assert case(32, 2048, 300) == (2048, True)
-    assert case(4, 2048, 300) == (2048, False)          # fewer than 8 requests
-    assert case(32, 128, 300) == (128, False)           # prefix below 256
-    assert case(32, 2048, 300, causal=False) == (2048, False)
+    assert case(64, 16384, 300) == (16384, True)        # 64 x 64 MB of prefix re-reads
+    assert case(4, 16384, 300) == (16384, False)        # fewer than 8 requests
+    assert case(64, 128, 300) == (128, False)           # prefix below 256
+    assert case(64, 16384, 300, causal=False) == (16384, False)
     assert case(8, 256, 100000)[1] is False             # saves 0.2 % of the bytes
+    assert case(32, 2048, 300)[1] is False              # the measured cascade_prefix shape
