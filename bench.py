@@ -356,6 +356,10 @@ def main():
                 one = measure(name, args, dev, flush, False, single_pass=True)
                 ent["single_pass_attn_avg_us"] = round(one["attn_mean_s"] * 1e6, 2)
                 ent["cascade_decision"] = {"common_prefix_len": P, "use_cascade": use}
+            if name == "chunked_prefill_mix":
+                ent["attn_TFLOPs"] = round(r["flops"] / r["attn_mean_s"] / 1e12, 1)
+                ent["mfma_frac"] = round(r["flops"] / r["attn_mean_s"] / 1e12 / BF16_PEAK_TFLOPS, 4)
+            sec[name] = ent
         if not fp8:
             # the decision on a longer shared prefix (64 requests x 16384 shared
             # tokens): both paths measured next to it
@@ -373,10 +377,6 @@ def main():
             sec[spec.name] = {"attn_avg_us": round(casc["attn_mean_s"] * 1e6, 2),
                               "single_pass_attn_avg_us": round(one["attn_mean_s"] * 1e6, 2),
                               "cascade_decision": {"common_prefix_len": P, "use_cascade": use}}
-            if name == "chunked_prefill_mix":
-                ent["attn_TFLOPs"] = round(r["flops"] / r["attn_mean_s"] / 1e12, 1)
-                ent["mfma_frac"] = round(r["flops"] / r["attn_mean_s"] / 1e12 / BF16_PEAK_TFLOPS, 4)
-            sec[name] = ent
         if not fp8:
             r = measure("decode_llama8b", args, dev, flush, False, fp8=True)
             sec["decode_llama8b_fp8"] = {
