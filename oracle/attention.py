@@ -24,6 +24,17 @@ What is computed, and where the pages define it:
   ``h // (H // Hkv)``; causal masking is bottom-right aligned (query i of a
   sequence with Lq queries and Lk keys sees keys ``j <= i + Lk - Lq``); a
   query that sees no key gets ``out = 0`` and ``lse = -inf``.
+* attention sinks (the ``s_aux`` argument of the FA3 path, "FlashAttention
+  在 vLLM 中的实现分析" section 1.2, a learnable sink token): one logit per
+  query head that joins the softmax denominator and carries no value:
+  ``out = sum_j e^{s_j} v_j / (sum_j e^{s_j} + e^{sink_h})`` and
+  ``lse = ln(sum_j e^{s_j} + e^{sink_h})``, where ``s_j`` are the scaled
+  scores (the sink is in the same units).  A row with no visible key gets
+  out = 0 and lse = sink_h.  Reading: the pages name the argument only.
+* sliding window (named among the cascade conditions, section 6.2): with a
+  window of W keys, query i sees keys ``i + Lk - Lq - (W - 1) <= j <= i + Lk - Lq``
+  (the causal bound and the W - 1 keys before it); W = 0 means no window.
+  Reading: the pages name the feature only; this is the usual decoder form.
 * ``merge_states`` / ``merge_attn_states``: LSE-weighted merge of partial
   attentions over disjoint key sets (section 6.3, step 3).
 * ``cascade_attention``: prefix pass (all queries as one pseudo-sequence,
@@ -119,7 +130,8 @@ def _softmax_rows(s: np.ndarray, vis: np.ndarray, v: np.ndarray):
 
 def varlen_attention(q: np.ndarray, kv_cache: np.ndarray, cu_seqlens_q: np.ndarray,
                      seqused_k: np.ndarray, block_table: np.ndarray, scale,
-                     causal: bool, num_kv_heads: int = None, k_scale=None, v_scale=None):
+                     causal: bool, num_kv_heads: int = None, k_scale=None, v_scale=None,
+                     s_aux=None, sliding_window: int = 0):
     """Paged varlen (GQA, optionally bottom-right causal) attention.
 
     q: bf16 bits [T, H, D]; kv_cache: bf16 bits (uint16) [2, NB, BS, Hkv, D],
@@ -127,7 +139,9 @@ def varlen_attention(q: np.ndarray, kv_cache: np.ndarray, cu_seqlens_q: np.ndarr
     fp32 dequantisation scales k_scale[Hkv], v_scale[Hkv] (key/value =
     E4M3 value * scale, see oracle.fp8);
     cu_seqlens_q: [B+1]; seqused_k: [B]; block_table: [B, max_blocks];
-    scale: the fp32 softmax scale (promoted exactly to fp64).
+    scale: the fp32 softmax scale (promoted exactly to fp64);
+    s_aux: None or fp32 [H] sink logits; sliding_window: W >= 0 keys (0 = none,
+    causal only).
     Returns out float64 [T, H, D] and lse float64 [T, H] (natural log)."""
     T, H, D = q.shape
     Hkv = kv_cache.shape[3] if num_kv_heads is None else num_kv_heads
@@ -155,10 +169,25 @@ def varlen_attention(q: np.ndarray, kv_cache: np.ndarray, cu_seqlens_q: np.ndarr
         else:
             K, V = bf16_to_f64(Kb), bf16_to_f64(Vb)
         vis = _visible(Lq, Lk, causal)
+        if sliding_window:
+            if not causal:
+                raise ValueError("a sliding window is defined for causal attention")
+            j = np.arange(Lk)[None, :]
+            i = np.arange(Lq)[:, None]
+            vis = vis & (j >= i + (Lk - Lq) - (int(sliding_window) - 1))
         for h in range(H):
             kvh = _kv_head(h, H, Hkv)
             s = scale * (qf[t0:t1, h, :] @ K[:, kvh, :].T)          # [Lq, Lk]
             o, l = _softmax_rows(s, vis, V[:, kvh, :])
+            if s_aux is not None:
+                # the sink's term joins the denominator: rescale by
+                # e^{lse} / (e^{lse} + e^{sink}), in a stable form
+                sink = float(np.float32(s_aux[h]))
+                M = np.maximum(l, sink)
+                a = np.where(np.isneginf(l), 0.0, np.exp(l - M))
+                b = np.exp(sink - M)
+                o = o * (a / (a + b))[:, None]
+                l = M + np.log(a + b)
             out[t0:t1, h] = o
             lse[t0:t1, h] = l
     return out, lse

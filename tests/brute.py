@@ -10,8 +10,11 @@ def bf16_bits_to_float(bits: int) -> float:
     return struct.unpack("<f", struct.pack("<I", (int(bits) & 0xFFFF) << 16))[0]
 
 
-def attention(q, kv_cache, cu_seqlens_q, seqused_k, block_table, scale, causal):
+def attention(q, kv_cache, cu_seqlens_q, seqused_k, block_table, scale, causal, window=0,
+              sinks=None):
     """q: nested/np uint16 [T][H][D]; kv_cache uint16 [2][NB][BS][Hkv][D].
+    window: W > 0 keeps keys last_visible - W + 1 .. last_visible; sinks: one
+    extra logit per head in the denominator (no value).
 
     Returns (out, lse) as nested Python lists of floats."""
     T = len(q)
@@ -36,6 +39,8 @@ def attention(q, kv_cache, cu_seqlens_q, seqused_k, block_table, scale, causal):
                 for j in range(n_k):
                     if j > last_visible:
                         continue
+                    if window and j < last_visible - window + 1:
+                        continue
                     blk = int(block_table[b][j // BS])
                     krow = kv_cache[0][blk][j % BS][g]
                     vrow = kv_cache[1][blk][j % BS][g]
@@ -43,11 +48,14 @@ def attention(q, kv_cache, cu_seqlens_q, seqused_k, block_table, scale, causal):
                                     for d in range(D))
                     scores.append(scale * dot)
                     rows.append(vrow)
+                sink = None if sinks is None else float(sinks[h])
                 if not scores:
+                    if sink is not None:
+                        lse[t][h] = sink
                     continue
-                mx = max(scores)
+                mx = max(scores + ([sink] if sink is not None else []))
                 w = [math.exp(s - mx) for s in scores]
-                den = math.fsum(w)
+                den = math.fsum(w + ([math.exp(sink - mx)] if sink is not None else []))
                 for d in range(D):
                     out[t][h][d] = math.fsum(w[j] * bf16_bits_to_float(rows[j][d])
                                              for j in range(len(w))) / den

@@ -352,4 +352,64 @@ def pin_reshape_and_cache():
         assert np.array_equal(after[1, phys, j % BS], Vb)
 
 
+def pin_sliding_window_brute_force():
+    for seed in range(4):
+        q, cache, cu, lk, bt, scale, causal = random_case(40 + seed, max_lk=45,
+                                                          allow_q_gt_k=(seed % 2 == 1))
+        for win in (1, 5, 17):
+            out, lse = OA.varlen_attention(q, cache, cu, lk, bt, scale, True, sliding_window=win)
+            bo, bl = brute.attention(q.tolist(), cache.tolist(), cu.tolist(), lk.tolist(),
+                                     bt.tolist(), float(scale), True, window=win)
+            _close(out, np.array(bo), 1e-12)
+            _close(lse, np.array(bl), 1e-12)
+
+
+def pin_sliding_window_limits():
+    """A window of one key returns that key's value; a window at least as
+    long as every context is no window."""
+    q, cache, cu, lk, bt, scale, causal = random_case(50, max_lk=30)
+    big = OA.varlen_attention(q, cache, cu, lk, bt, scale, True, sliding_window=1000)
+    full = OA.varlen_attention(q, cache, cu, lk, bt, scale, True)
+    _close(big[0], full[0], 0.0)
+    _close(big[1], full[1], 0.0)
+    out, lse = OA.varlen_attention(q, cache, cu, lk, bt, scale, True, sliding_window=1)
+    H = q.shape[1]
+    for b in range(len(lk)):
+        Lq, Lk = int(cu[b + 1] - cu[b]), int(lk[b])
+        for i in range(Lq):
+            j = i + Lk - Lq
+            if j < 0:
+                assert np.isneginf(lse[cu[b] + i]).all()
+                continue
+            K, V = OA.gather_kv(cache, bt[b], Lk)
+            for h in range(H):
+                kvh = h // (H // cache.shape[3])
+                assert np.allclose(out[cu[b] + i, h], OA.bf16_to_f64(V[j, kvh]), atol=1e-12)
+
+
+def pin_sinks_brute_force():
+    rng = np.random.default_rng(60)
+    for seed in range(4):
+        q, cache, cu, lk, bt, scale, causal = random_case(60 + seed, allow_q_gt_k=(seed % 2 == 0))
+        sinks = rng.standard_normal(q.shape[1]).astype(np.float32) * 2
+        out, lse = OA.varlen_attention(q, cache, cu, lk, bt, scale, causal, s_aux=sinks)
+        bo, bl = brute.attention(q.tolist(), cache.tolist(), cu.tolist(), lk.tolist(),
+                                 bt.tolist(), float(scale), causal, sinks=sinks.tolist())
+        _close(out, np.array(bo), 1e-12)
+        _close(lse, np.array(bl), 1e-12)
+
+
+def pin_sinks_are_a_merge_with_an_empty_state():
+    """A sink equals merging the attention with a state of out = 0 and
+    lse = sink (a key with logit sink and value 0)."""
+    q, cache, cu, lk, bt, scale, causal = random_case(70, allow_q_gt_k=True)
+    sinks = np.array([0.5, -3.0, 4.0, 0.0], np.float32)
+    out, lse = OA.varlen_attention(q, cache, cu, lk, bt, scale, True, s_aux=sinks)
+    o0, l0 = OA.varlen_attention(q, cache, cu, lk, bt, scale, True)
+    T, H, D = o0.shape
+    mo, ml = OA.merge_states([o0, np.zeros_like(o0)], [l0, np.broadcast_to(sinks, (T, H))])
+    _close(out, mo, 1e-12)
+    _close(lse, ml, 1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -73,8 +73,24 @@ def _merge_log2(outs, lses):
     return o, np.where(np.isneginf(l), l, M + np.log2(np.exp(l - np.where(np.isneginf(M), 0, M))))
 
 
-def _scale_dropped(q, kv_cache, cu, sk, bt, scale, causal, num_kv_heads=None):
-    return _orig_varlen(q, kv_cache, cu, sk, bt, 1.0, causal, num_kv_heads)
+def _scale_dropped(q, kv_cache, cu, sk, bt, scale, causal, num_kv_heads=None, **kw):
+    return _orig_varlen(q, kv_cache, cu, sk, bt, 1.0, causal, num_kv_heads, **kw)
+
+
+def _window_off_by_one(*args, sliding_window=0, **kw):
+    return _orig_varlen(*args, sliding_window=(sliding_window + 1 if sliding_window else 0), **kw)
+
+
+def _sink_dropped(*args, s_aux=None, **kw):
+    return _orig_varlen(*args, **kw)
+
+
+def _sink_as_value_one(*args, s_aux=None, **kw):
+    out, lse = _orig_varlen(*args, s_aux=s_aux, **kw)
+    if s_aux is None:
+        return out, lse
+    sink = np.asarray(s_aux, dtype=np.float64)[None, :]
+    return out + np.exp(sink - lse)[..., None], lse
 
 
 MUTANTS = {
@@ -89,6 +105,9 @@ MUTANTS = {
     "merge_unweighted": ("merge_states", _merge_no_weights),
     "merge_log2": ("merge_states", _merge_log2),
     "scale_dropped": ("varlen_attention", _scale_dropped),
+    "window_off_by_one": ("varlen_attention", _window_off_by_one),
+    "sink_dropped": ("varlen_attention", _sink_dropped),
+    "sink_carries_a_value": ("varlen_attention", _sink_as_value_one),
 }
 
 
