@@ -78,6 +78,8 @@ typedef struct {
   int32_t block_table_stride;
   int32_t causal;
   float scale;
+  int32_t sliding_window;   /* 0: none; W > 0 (causal only): query i sees keys
+                               i + Lk - Lq - (W - 1) .. i + Lk - Lq */
 } pa_attn_params;
 
 /* ------------------------------------------------------------------------
@@ -112,6 +114,7 @@ typedef struct {
   int32_t num_partial_rows;  /* fp32 partial rows held in the workspace      */
   int32_t max_reduce_rows;   /* most rows of any reduce item                 */
   int32_t batch, num_heads, num_kv_heads, head_size, causal, num_tokens;
+  int32_t sliding_window;    /* as planned (item key ranges start at the window) */
   size_t worklist_bytes;
   size_t workspace_bytes;
 } pa_plan_info;
@@ -290,6 +293,41 @@ pa_status pa_varlen_fwd_fp8(const pa_attn_params* p, const pa_plan_info* plan,
                             const float* k_scale, const float* v_scale,
                             int32_t num_tokens, void* out, float* lse,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * pa_varlen_fwd_ex -- pa_varlen_fwd with the options of the FA3 path the
+ * pages list ("FlashAttention 在 vLLM 中的实现分析", section 1.2: the s_aux
+ * argument, a learnable attention sink; the FP8 KV cache above):
+ *
+ *   kv_dtype   PA_KV_BF16 (the bf16 cache) or PA_KV_E4M3 (the E4M3 cache,
+ *              with k_scale / v_scale as for pa_varlen_fwd_fp8)
+ *   s_aux      NULL, or device fp32 [num_heads]: one sink logit per query
+ *              head, in the units of the scaled scores, that joins each
+ *              row's softmax denominator and carries no value:
+ *                out = sum_j e^{s_j} v_j / (sum_j e^{s_j} + e^{s_aux[h]}),
+ *                lse = ln(sum_j e^{s_j} + e^{s_aux[h]});
+ *              a row that sees no key gets out = 0, lse = s_aux[h].  In a
+ *              cascade give it to one of the two passes only.
+ * The sliding window is a shape parameter (pa_attn_params.sliding_window)
+ * and must equal the planned one.  Same errors as pa_varlen_fwd.
+ * ------------------------------------------------------------------------ */
+#define PA_KV_BF16 0
+#define PA_KV_E4M3 1
+
+typedef struct {
+  int32_t kv_dtype;
+  const float* k_scale;
+  const float* v_scale;
+  const float* s_aux;
+} pa_fwd_options;
+
+pa_status pa_varlen_fwd_ex(const pa_attn_params* p, const pa_plan_info* plan,
+                           const int32_t* worklist,
+                           const void* q, const void* kv_cache,
+                           const int32_t* cu_seqlens_q, const int32_t* seqused_k,
+                           const int32_t* block_table, const pa_fwd_options* opt,
+                           int32_t num_tokens, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * pa_merge_attn_states -- LSE-weighted merge of two partial attentions over

@@ -179,7 +179,24 @@ struct AttnArgs {
   float scale_log2;   // scale * log2(e)
   const float* k_scale;   // E4M3 cache: per-KV-head dequantisation scales
   const float* v_scale;
+  const float* s_aux;     // per-query-head sink logits, or null
+  int window;             // sliding window W (0: none)
 };
+
+// The sink's share of the denominator, added where a row's final state is
+// formed (never to split partials: their merge adds it once).  m: the row's
+// reference max, l / lr: its sums relative to m, all in the log2 domain.
+// Returns the factor that rescales O (relative to m) and replaces m, l, lr
+// by the sink-inclusive values relative to the new reference.
+__device__ __forceinline__ float add_sink(float sink_l2, float& m, float& l, float& lr) {
+  const float M = fmaxf(m, sink_l2);
+  const float a = (m == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(m - M);
+  const float b = __builtin_amdgcn_exp2f(sink_l2 - M);
+  m = M;
+  l = l * a + b;
+  lr = lr * a + b;
+  return a;
+}
 
 // ---------------------------------------------------------------------------
 // reshape_and_cache: one thread per 16-byte chunk; consecutive threads take
@@ -316,6 +333,7 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
   const int tok = r / G;
   const int head = it.kvh * G + (r - tok * G);
   const int row_limit = a.causal ? tok + Lk - Lq : INT_MAX;
+  const int row_lo = a.window > 0 ? tok + Lk - Lq - (a.window - 1) : INT_MIN;
   // an E4M3 cache holds K / k_scale and V / v_scale of each KV head: the
   // scores take k_scale inside the exponent's factor, O takes v_scale at the end
   const float sl2 = FP8 ? a.scale_log2 * ld_uniform(a.k_scale + it.kvh) : a.scale_log2;
@@ -421,7 +439,7 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = kb + 4 * g + i;
-        x[i] = (key >= kv1 || key > row_limit) ? kNegInf : s[i] * sl2;
+        x[i] = (key >= kv1 || key > row_limit || key < row_lo) ? kNegInf : s[i] * sl2;
       }
       float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       mx = wave_max_xor(mx, 16);
@@ -490,8 +508,13 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
       L += wt[w] * sl[w * 16 + er];
       Lr += wt[w] * sr[w * 16 + er];
     }
+    const int rr = it.row0 + er;
+    const int etok = rr / G;
+    const int ehead = it.kvh * G + (rr - etok * G);
+    float fo = 1.f;      // rescales the weighted O when a sink moves the reference
+    if (a.s_aux && it.prow < 0) fo = add_sink(a.s_aux[ehead] * kLog2e, M, L, Lr);
     const bool empty = !(L > 0.f);
-    const float inv = empty ? 0.f : vsc / Lr;
+    const float inv = empty ? 0.f : vsc * fo / Lr;
     const float lse_v = empty ? kNegInf : (M + __log2f(L)) * kLn2;
     float acc[DPT];
 #pragma unroll
@@ -501,9 +524,6 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
       for (int w = 0; w < 4; ++w) sum += wt[w] * so[(w * 16 + er) * D + ec * DPT + e];
       acc[e] = sum * inv;
     }
-    const int rr = it.row0 + er;
-    const int etok = rr / G;
-    const int ehead = it.kvh * G + (rr - etok * G);
     if (it.prow < 0) {
       const int64_t orow = (int64_t)(t0 + etok) * a.H + ehead;
       uint16_t* op = a.out + orow * D + ec * DPT;
@@ -602,8 +622,11 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
   // scores take k_scale inside the exponent's factor, O takes v_scale at the end
   const float sl2 = FP8 ? a.scale_log2 * ld_uniform(a.k_scale + it.kvh) : a.scale_log2;
   const float vsc = FP8 ? ld_uniform(a.v_scale + it.kvh) : 1.f;
-  // every row of this wave sees keys up to at least wave_limit
+  // every row of this wave sees keys up to at least wave_limit, and (with a
+  // sliding window) no row of it sees a key below wave_lo
   const int wave_limit = a.causal ? (it.row0 + wave * 32) / G + Lk - Lq : INT_MAX;
+  const int wave_lo = a.window > 0 ? (it.row0 + wave * 32 + 31) / G + Lk - Lq - (a.window - 1) : INT_MIN;
+  const int row_lo = a.window > 0 ? tok + Lk - Lq - (a.window - 1) : INT_MIN;
 
   bf16x8_t qf[NKT];
   if (row_ok) {
@@ -762,12 +785,17 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
     // the last visible key of this lane's row, relative to the lane's first
     // key j0 + 4h, so that each element compares a compile-time offset
     const int lim = min(kv1 - 1, row_limit) - j0 - 4 * h;
+    // the first key of the row's sliding window, relative likewise
+    const int lim_lo = (row_lo == INT_MIN) ? INT_MIN : row_lo - j0 - 4 * h;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float v = s[u][i];
-        if constexpr (MASKED) v = (32 * u + 8 * (i >> 2) + (i & 3) > lim) ? kNegInf : v;
+        if constexpr (MASKED) {
+          const int off = 32 * u + 8 * (i >> 2) + (i & 3);
+          v = (off > lim || off < lim_lo) ? kNegInf : v;
+        }
         x[16 * u + i] = v;
       }
     float mx = x[0];
@@ -848,7 +876,7 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
   for (; j0 < kv1; j0 += 64, buf ^= 1) {
     const bool more = j0 + 64 < kv1;
     if (more) load_any(j0 + 64);
-    if (j0 + 64 > kv1 || j0 + 63 > wave_limit)
+    if (j0 + 64 > kv1 || j0 + 63 > wave_limit || j0 < wave_lo)
       tile(j0, buf, Bool<true>{});
     else
       tile(j0, buf, Bool<false>{});
@@ -859,8 +887,10 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
   l_run += __shfl_xor(l_run, 32);
   lr_run += __shfl_xor(lr_run, 32);
   if (!row_ok) return;
+  float fo = 1.f;      // rescales O when a sink moves the reference
+  if (a.s_aux && it.prow < 0) fo = add_sink(a.s_aux[head] * kLog2e, m_run, l_run, lr_run);
   const bool empty = !(l_run > 0.f);
-  const float inv = empty ? 0.f : vsc / lr_run;
+  const float inv = empty ? 0.f : vsc * fo / lr_run;
   const float lse_v = empty ? kNegInf : (m_run + __log2f(l_run)) * kLn2;
   // lane (n, h) reg i of tile dt holds O^T[d = 32dt + 8(i/4) + 4h + i%4][row n]
   if (it.prow < 0) {
@@ -926,7 +956,7 @@ template <int D>
 __global__ __launch_bounds__(256) void split_reduce_kernel(
     const int32_t* __restrict__ ritems, const float* __restrict__ part_o,
     const float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse, int H,
-    int G) {
+    int G, const float* __restrict__ s_aux) {
   constexpr int EPL = D / 64;
   static_assert(EPL >= 1, "split reduce");
   __shared__ float s_m[4], s_l[4];
@@ -968,22 +998,28 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(
   }
   __syncthreads();
   if (wave != 0) return;
-  const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  const int rr = row0 + row;
+  const int tok = rr / G;
+  const int head = kvh * G + (rr - tok * G);
+  float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
   float w[4], Lt = 0.f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     w[k] = (s_m[k] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(s_m[k] - M);
     Lt += w[k] * s_l[k];
   }
+  // a sink joins the merged denominator once (the partials exclude it)
+  float fo = 1.f;
+  if (s_aux) {
+    float unused = 0.f;
+    fo = add_sink(ld_uniform(s_aux + head) * kLog2e, M, Lt, unused);
+  }
   const bool empty = !(Lt > 0.f);
-  const float inv = empty ? 0.f : 1.f / Lt;
+  const float inv = empty ? 0.f : fo / Lt;
 #pragma unroll
   for (int e = 0; e < EPL; ++e)
     acc[e] = ((w[0] * s_o[0][lane * EPL + e] + w[1] * s_o[1][lane * EPL + e]) +
               (w[2] * s_o[2][lane * EPL + e] + w[3] * s_o[3][lane * EPL + e])) * inv;
-  const int rr = row0 + row;
-  const int tok = rr / G;
-  const int head = kvh * G + (rr - tok * G);
   const int64_t orow = (int64_t)(t0 + tok) * H + head;
   uint16_t* op = out + orow * D + lane * EPL;
   if constexpr (EPL == 1) {
@@ -1057,7 +1093,8 @@ pa_status launch_fwd(const AttnArgs& base, const pa_plan_info* plan, const int32
         items + (int64_t)(plan->num_small_items + plan->num_tiled_items) * PA_ITEM_WORDS;
     hipLaunchKernelGGL(split_reduce_kernel<D>, dim3(plan->num_reduce_items, plan->max_reduce_rows),
                        dim3(256), 0, stream,
-                       r, base.part_o, base.part_lse, base.out, base.lse, base.H, base.G);
+                       r, base.part_o, base.part_lse, base.out, base.lse, base.H, base.G,
+                       base.s_aux);
   }
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
@@ -1134,14 +1171,16 @@ namespace {
 pa_status varlen_fwd(const pa_attn_params* p, const pa_plan_info* plan, const int32_t* worklist,
                      const void* q, const void* kv_cache, const int32_t* cu_seqlens_q,
                      const int32_t* seqused_k, const int32_t* block_table, const float* k_scale,
-                     const float* v_scale, bool fp8, int32_t num_tokens, void* out, float* lse,
-                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                     const float* v_scale, bool fp8, const float* s_aux, int32_t num_tokens,
+                     void* out, float* lse, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
   pa_status st = pa::check_params(p);
   if (st != PA_OK) return st;
   if (!plan) return PA_ERR_INVALID_ARGUMENT;
   if (plan->batch != p->batch || plan->num_heads != p->num_heads ||
       plan->num_kv_heads != p->num_kv_heads || plan->head_size != p->head_size ||
-      plan->causal != p->causal || plan->num_tokens != num_tokens)
+      plan->causal != p->causal || plan->num_tokens != num_tokens ||
+      plan->sliding_window != p->sliding_window)
     return PA_ERR_INVALID_ARGUMENT;
   if (plan->num_small_items < 0 || plan->num_tiled_items < 0 || plan->num_reduce_items < 0 ||
       plan->num_partial_rows < 0 || plan->max_reduce_rows < 0 ||
@@ -1159,6 +1198,7 @@ pa_status varlen_fwd(const pa_attn_params* p, const pa_plan_info* plan, const in
     return PA_ERR_INVALID_ARGUMENT;
   if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
     return PA_ERR_INVALID_ARGUMENT;
+  if (s_aux && !aligned(s_aux, 4)) return PA_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(worklist, 4) ||
       (lse && !aligned(lse, 4)))
     return PA_ERR_INVALID_ARGUMENT;
@@ -1192,6 +1232,8 @@ pa_status varlen_fwd(const pa_attn_params* p, const pa_plan_info* plan, const in
   a.scale_log2 = p->scale * kLog2e;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  a.s_aux = s_aux;
+  a.window = p->sliding_window;
   switch (p->head_size) {
     case 64: return fp8 ? launch_fwd<64, true>(a, plan, worklist, stream)
                         : launch_fwd<64, false>(a, plan, worklist, stream);
@@ -1213,7 +1255,21 @@ pa_status pa_varlen_fwd(const pa_attn_params* p, const pa_plan_info* plan, const
                         void* out, float* lse, void* workspace, size_t workspace_bytes,
                         hipStream_t stream) {
   return varlen_fwd(p, plan, worklist, q, kv_cache, cu_seqlens_q, seqused_k, block_table, nullptr,
-                    nullptr, false, num_tokens, out, lse, workspace, workspace_bytes, stream);
+                    nullptr, false, nullptr, num_tokens, out, lse, workspace, workspace_bytes,
+                    stream);
+}
+
+pa_status pa_varlen_fwd_ex(const pa_attn_params* p, const pa_plan_info* plan,
+                           const int32_t* worklist, const void* q, const void* kv_cache,
+                           const int32_t* cu_seqlens_q, const int32_t* seqused_k,
+                           const int32_t* block_table, const pa_fwd_options* opt,
+                           int32_t num_tokens, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  if (!opt || (opt->kv_dtype != PA_KV_BF16 && opt->kv_dtype != PA_KV_E4M3))
+    return PA_ERR_INVALID_ARGUMENT;
+  return varlen_fwd(p, plan, worklist, q, kv_cache, cu_seqlens_q, seqused_k, block_table,
+                    opt->k_scale, opt->v_scale, opt->kv_dtype == PA_KV_E4M3, opt->s_aux,
+                    num_tokens, out, lse, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_varlen_fwd_fp8(const pa_attn_params* p, const pa_plan_info* plan,
@@ -1223,7 +1279,8 @@ pa_status pa_varlen_fwd_fp8(const pa_attn_params* p, const pa_plan_info* plan,
                             int32_t num_tokens, void* out, float* lse, void* workspace,
                             size_t workspace_bytes, hipStream_t stream) {
   return varlen_fwd(p, plan, worklist, q, kv_cache, cu_seqlens_q, seqused_k, block_table, k_scale,
-                    v_scale, true, num_tokens, out, lse, workspace, workspace_bytes, stream);
+                    v_scale, true, nullptr, num_tokens, out, lse, workspace, workspace_bytes,
+                    stream);
 }
 
 pa_status pa_merge_attn_states(void* out, float* out_lse, const void* prefix_out,

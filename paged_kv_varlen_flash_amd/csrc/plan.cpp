@@ -40,6 +40,8 @@ pa_status check_params(const pa_attn_params* p) {
     return PA_ERR_INVALID_ARGUMENT;
   if ((int64_t)p->max_blocks_per_seq * p->block_size > INT32_MAX / 2) return PA_ERR_INVALID_ARGUMENT;
   if (p->causal != 0 && p->causal != 1) return PA_ERR_INVALID_ARGUMENT;
+  // a sliding window is the causal band of its last W keys
+  if (p->sliding_window < 0 || (p->sliding_window > 0 && !p->causal)) return PA_ERR_INVALID_ARGUMENT;
   // a softmax scale is positive (the kernels take row maxima on unscaled scores)
   if (!std::isfinite(p->scale) || !(p->scale > 0.f)) return PA_ERR_INVALID_ARGUMENT;
   // byte offsets into the cache must fit in 64 bits with room to spare, and
@@ -54,6 +56,7 @@ namespace {
 struct Unit {        // one (sequence, kv head, row block) with its visible key range
   int32_t seq, kvh, row0, nrows, kv_end;
   bool small;
+  int32_t kv_begin;  // first key any row of the block sees (a multiple of 16)
 };
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -136,15 +139,23 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
           const int64_t i_last = (r0 + nr - 1) / G;
           kv_end = std::min<int64_t>(Lk, std::max<int64_t>(0, i_last + Lk - Lq + 1));
         }
-        units.push_back(Unit{b, kvh, r0, nr, (int32_t)kv_end, small});
+        int64_t kv_begin = 0;
+        if (p->sliding_window > 0) {
+          // the block's first query token i sees keys j >= i + Lk - Lq - (W - 1);
+          // ranges start on a multiple of 16 (one cache block per 16 keys)
+          const int64_t i_first = r0 / G;
+          const int64_t lo = i_first + Lk - Lq - (p->sliding_window - 1);
+          kv_begin = std::min<int64_t>(std::max<int64_t>(lo, 0), kv_end) / 16 * 16;
+        }
+        units.push_back(Unit{b, kvh, r0, nr, (int32_t)kv_end, small, (int32_t)kv_begin});
       }
   }
 
   // ---- split-KV choice
   int64_t small_keys = 0, tiled_keys = 0, n_tiled = 0, n_small = 0;
   for (const Unit& u : units) {
-    if (u.small) { small_keys += u.kv_end; ++n_small; }
-    else { tiled_keys += u.kv_end; ++n_tiled; }
+    if (u.small) { small_keys += u.kv_end - u.kv_begin; ++n_small; }
+    else { tiled_keys += u.kv_end - u.kv_begin; ++n_tiled; }
   }
   const int64_t target = PA_PLAN_TARGET_CUS;
   int64_t tiled_chunk = 0;
@@ -185,7 +196,7 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
     for (const Unit& u : units) {
       if (!u.small) continue;
       const size_t first = small_items.size();
-      const int32_t kv = u.kv_end;
+      const int32_t kv = u.kv_end - u.kv_begin;
       int32_t c = kv;
       if (kv > 0) {
         if (force_splits > 0) {
@@ -195,16 +206,16 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
           c = ceil_div32(ceil_div32(kv, nsp), 64) * 64;
         }
       }
-      int32_t k0 = 0;
+      int32_t k0 = u.kv_begin;
       do {
-        const int32_t k1 = std::min(kv, k0 + std::max(c, 1));
+        const int32_t k1 = std::min(u.kv_end, k0 + std::max(c, 1));
         // cost: an estimate of the workgroup's time, comparable with the
         // tiled items' (a small-row workgroup streams a key about as fast as
         // a full 128-row tiled one computes it)
         small_items.push_back(
             Item{{u.seq, u.kvh, u.row0, u.nrows, k0, k1, -1, 0}, (int64_t)(k1 - k0) * PA_TILED_ROWS});
         k0 = k1;
-      } while (k0 < kv);
+      } while (k0 < u.kv_end);
       if (!finish_unit(u, small_items, first)) return PA_ERR_INVALID_ARGUMENT;
     }
   }
@@ -217,7 +228,7 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
     // (32-bit arithmetic: key counts are below 2^30, and 64-bit divisions
     // would dominate the planner's time)
     const int32_t align = force_splits > 0 ? 16 : kKeyTile;
-    const int32_t kv = u.kv_end;
+    const int32_t kv = u.kv_end - u.kv_begin;
     int32_t chunk = kv;
     if (kv > 0) {
       if (force_splits > 0) {
@@ -230,13 +241,13 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
       chunk = std::max(chunk, align);
     }
     const size_t first = tiled_items.size();
-    int32_t k0 = 0;
+    int32_t k0 = u.kv_begin;
     do {
-      const int32_t k1 = std::min(kv, k0 + chunk);
+      const int32_t k1 = std::min(u.kv_end, k0 + chunk);
       tiled_items.push_back(
           Item{{u.seq, u.kvh, u.row0, u.nrows, k0, k1, -1, 1}, (int64_t)(k1 - k0) * u.nrows});
       k0 = k1;
-    } while (k0 < kv);
+    } while (k0 < u.kv_end);
     if (!finish_unit(u, tiled_items, first)) return PA_ERR_INVALID_ARGUMENT;
   }
   const size_t n_items = small_items.size() + tiled_items.size() + reduce_items.size();
@@ -252,6 +263,7 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
   info->num_kv_heads = Hkv;
   info->head_size = p->head_size;
   info->causal = p->causal;
+  info->sliding_window = p->sliding_window;
   info->num_tokens = T;
   info->worklist_bytes = words * sizeof(int32_t);
   // partial rows: fp32 [prow, D] values, then fp32 [prow] lse, 256-B aligned
@@ -348,7 +360,7 @@ pa_status pa_cascade_decide(const pa_attn_params* p, const int32_t* cu, const in
   }
   const int64_t P = nblk * BS;
   *common_prefix_len = (int32_t)P;
-  if (!p->causal || P < 256 || B < 8) return PA_OK;
+  if (!p->causal || p->sliding_window != 0 || P < 256 || B < 8) return PA_OK;
 
   // cost model: plan both paths and price their launches with times fitted
   // to MI355X measurements of this library (microseconds)
@@ -416,7 +428,7 @@ pa_status pa_cascade_split(const pa_attn_params* p, int32_t common_prefix_len,
   if (st != PA_OK) return st;
   if (!prefix_p || !suffix_p || !prefix_cu || !prefix_sk || !col0) return PA_ERR_INVALID_ARGUMENT;
   if (p->batch > 0 && (!cu || !sk || !suffix_sk)) return PA_ERR_INVALID_ARGUMENT;
-  if (p->causal != 1) return PA_ERR_INVALID_ARGUMENT;
+  if (p->causal != 1 || p->sliding_window != 0) return PA_ERR_INVALID_ARGUMENT;
   const int32_t BS = p->block_size;
   if (common_prefix_len <= 0 || common_prefix_len % BS != 0) return PA_ERR_INVALID_ARGUMENT;
   const int32_t nblk = common_prefix_len / BS;

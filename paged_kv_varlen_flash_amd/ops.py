@@ -34,7 +34,8 @@ PLAN_TARGET_CUS = 256          # compute units the planner schedules for (PA_PLA
 
 EXPORTED = ["pa_status_str", "pa_version", "pa_supported_head_sizes", "pa_plan_varlen",
             "pa_cascade_split", "pa_reshape_and_cache", "pa_varlen_fwd", "pa_merge_attn_states",
-            "pa_reshape_and_cache_fp8", "pa_varlen_fwd_fp8", "pa_cascade_decide"]
+            "pa_reshape_and_cache_fp8", "pa_varlen_fwd_fp8", "pa_cascade_decide",
+            "pa_varlen_fwd_ex"]
 
 
 class PaError(RuntimeError):
@@ -48,7 +49,8 @@ class AttnParams(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_size", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
                 ("max_blocks_per_seq", ctypes.c_int32), ("block_table_stride", ctypes.c_int32),
-                ("causal", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("sliding_window", ctypes.c_int32)]
 
     def __repr__(self):
         return "AttnParams(" + ", ".join(f"{k}={getattr(self, k)}" for k, _ in self._fields_) + ")"
@@ -61,10 +63,19 @@ class PlanInfo(ctypes.Structure):
                 ("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_size", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
+                ("sliding_window", ctypes.c_int32),
                 ("worklist_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+PA_KV_BF16, PA_KV_E4M3 = 0, 1
+
+
+class FwdOptions(ctypes.Structure):
+    _fields_ = [("kv_dtype", ctypes.c_int32), ("k_scale", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p), ("s_aux", ctypes.c_void_p)]
 
 
 _lib = None
@@ -107,6 +118,10 @@ def lib() -> ctypes.CDLL:
         L.pa_varlen_fwd_fp8.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(PlanInfo), _P,
                                         _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P,
                                         ctypes.c_size_t, _P]
+        L.pa_varlen_fwd_ex.restype = ctypes.c_int
+        L.pa_varlen_fwd_ex.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(PlanInfo), _P,
+                                       _P, _P, _P, _P, _P, ctypes.POINTER(FwdOptions),
+                                       ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P]
         L.pa_merge_attn_states.restype = ctypes.c_int
         L.pa_merge_attn_states.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int32, _P]
@@ -137,10 +152,12 @@ def _ptr_i32(a: Optional[np.ndarray]):
 
 
 def make_params(batch, num_heads, num_kv_heads, head_size, block_size, num_blocks,
-                max_blocks_per_seq, causal, scale, block_table_stride=0) -> AttnParams:
+                max_blocks_per_seq, causal, scale, block_table_stride=0,
+                sliding_window=0) -> AttnParams:
     return AttnParams(int(batch), int(num_heads), int(num_kv_heads), int(head_size),
                       int(block_size), int(num_blocks), int(max_blocks_per_seq),
-                      int(block_table_stride), int(bool(causal)), float(np.float32(scale)))
+                      int(block_table_stride), int(bool(causal)), float(np.float32(scale)),
+                      int(sliding_window))
 
 
 # --------------------------------------------------------------------------
@@ -283,6 +300,27 @@ def pa_varlen_fwd_fp8(params: AttnParams, plan: PlanInfo, worklist, q, kv_cache,
     _check(st, "pa_varlen_fwd_fp8")
 
 
+def pa_varlen_fwd_ex(params: AttnParams, plan: PlanInfo, worklist, q, kv_cache, cu_seqlens_q,
+                     seqused_k, block_table, out, lse=None, workspace=None, stream=None,
+                     k_scale=None, v_scale=None, s_aux=None):
+    """bf16 cache, or (k_scale and v_scale given) a uint8 E4M3 cache;
+    s_aux: None or fp32 [H] sink logits."""
+    import torch
+    fp8 = k_scale is not None or v_scale is not None
+    opt = FwdOptions(PA_KV_E4M3 if fp8 else PA_KV_BF16,
+                     _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
+                     _dev(s_aux, "s_aux", torch.float32))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().pa_varlen_fwd_ex(
+        ctypes.byref(params), ctypes.byref(plan), _dev(worklist, "worklist", torch.int32),
+        _dev(q, "q", torch.bfloat16), _dev(kv_cache, "kv_cache", torch.uint8 if fp8 else torch.bfloat16),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(seqused_k, "seqused_k", torch.int32),
+        _dev(block_table, "block_table", torch.int32), ctypes.byref(opt), int(q.shape[0]),
+        _dev(out, "out", torch.bfloat16), _dev(lse, "lse", torch.float32),
+        _dev(workspace, "workspace"), ws_bytes, _stream(stream))
+    _check(st, "pa_varlen_fwd_ex")
+
+
 def pa_merge_attn_states(out, out_lse, prefix_out, prefix_lse, suffix_out, suffix_lse,
                          stream=None):
     import torch
@@ -320,25 +358,31 @@ class VarlenPlan:
 
 
 def plan_varlen(q_shape, kv_cache_shape, block_table_shape, host_cu_seqlens_q, host_seqused_k,
-                scale, causal, force_splits=0, block_table_stride=0) -> VarlenPlan:
+                scale, causal, force_splits=0, block_table_stride=0,
+                sliding_window=0) -> VarlenPlan:
     T, H, D = q_shape
     _, NB, BS, Hkv, D2 = kv_cache_shape
     if D2 != D:
         raise ValueError("head size of q and kv_cache differ")
     B, MB = block_table_shape
-    p = make_params(B, H, Hkv, D, BS, NB, MB, causal, scale, block_table_stride)
+    p = make_params(B, H, Hkv, D, BS, NB, MB, causal, scale, block_table_stride, sliding_window)
     return VarlenPlan(p, host_cu_seqlens_q, host_seqused_k, force_splits)
 
 
 def varlen_fwd(q, kv_cache, cu_seqlens_q, seqused_k, block_table, plan: VarlenPlan,
-               out=None, lse=None, stream=None, k_scale=None, v_scale=None):
-    """bf16 cache, or (k_scale and v_scale given) a uint8 E4M3 cache."""
+               out=None, lse=None, stream=None, k_scale=None, v_scale=None, s_aux=None):
+    """bf16 cache, or (k_scale and v_scale given) a uint8 E4M3 cache;
+    s_aux: optional fp32 [H] sink logits."""
     import torch
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
-    if k_scale is None and v_scale is None:
+    if s_aux is not None:
+        pa_varlen_fwd_ex(plan.params, plan.info, plan.worklist, q, kv_cache, cu_seqlens_q,
+                         seqused_k, block_table, out, lse, plan.workspace, stream,
+                         k_scale, v_scale, s_aux)
+    elif k_scale is None and v_scale is None:
         pa_varlen_fwd(plan.params, plan.info, plan.worklist, q, kv_cache, cu_seqlens_q, seqused_k,
                       block_table, out, lse, plan.workspace, stream)
     else:

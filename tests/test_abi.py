@@ -416,3 +416,73 @@ def test_cascade_decide_thresholds(L):
     assert case(64, 16384, 300, causal=False) == (16384, False)
     assert case(8, 256, 100000)[1] is False             # saves 0.2 % of the bytes
     assert case(32, 2048, 300)[1] is False              # the measured cascade_prefix shape
+
+
+# ---------------------------------------------------------------- sliding window plans
+@pytest.mark.parametrize("seed", range(6))
+def test_plan_covers_sliding_window(L, seed):
+    """With a window of W keys, each row block's ranges start at a multiple of
+    16 at or below its first row's window start and still tile up to the
+    block's causal end; every visible key of every row is covered."""
+    rng = np.random.default_rng(900 + seed)
+    G = int(rng.choice([1, 4, 8]))
+    Hkv = 2
+    B = 6
+    q_lens = rng.integers(1, 300, B).astype(np.int32)
+    q_lens[::2] = 1                                   # decode rows too
+    k_lens = (q_lens + rng.integers(0, 2000, B)).astype(np.int32)
+    W_ = int(rng.choice([1, 16, 100, 1000]))
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    BS = 16
+    MB = int((k_lens.max() + BS - 1) // BS)
+    force = int(rng.choice([0, 3]))
+    p = ops.make_params(B, G * Hkv, Hkv, 64, BS, 40000, MB, True, 0.1, sliding_window=W_)
+    words, info = ops.pa_plan_varlen(p, cu, k_lens, force)
+    assert info.sliding_window == W_
+    items, red = parse(words, info)
+    cover = {}
+    for seq, kvh, row0, nrows, k0, k1, prow, word7 in items:
+        assert k0 % 16 == 0
+        for r in range(row0, row0 + nrows):
+            cover.setdefault((seq, kvh, r), []).append((k0, k1))
+    for b in range(B):
+        Lq, Lk = int(q_lens[b]), int(k_lens[b])
+        for kvh in range(Hkv):
+            for r in range(Lq * G):
+                ranges = sorted(cover[(b, kvh, r)])
+                i = r // G
+                hi = min(Lk - 1, i + Lk - Lq)
+                lo = max(0, i + Lk - Lq - (W_ - 1))
+                pos = ranges[0][0]
+                assert pos <= max(lo, 0) or hi < lo
+                for k0, k1 in ranges:
+                    assert k0 == pos
+                    pos = k1
+                assert pos >= hi + 1 or hi < lo
+
+
+def test_window_params_validation(L):
+    E = ops.PA_ERR_INVALID_ARGUMENT
+    cu = np.array(CU, np.int32)
+    sk = np.array(SK, np.int32)
+    info = ops.PlanInfo()
+    for causal, W_ in ((False, 16), (True, -1)):
+        p = ops.make_params(len(SK), 8, 2, 64, 16, 64, 8, causal, 0.1, sliding_window=W_)
+        st = L.pa_plan_varlen(ctypes.byref(p), cu.ctypes.data_as(ops._I32P),
+                              sk.ctypes.data_as(ops._I32P), 0, None, 0, ctypes.byref(info))
+        assert st == E
+    # a plan made without the window does not serve a call with one
+    p = params()
+    _, info = ops.pa_plan_varlen(p, CU, SK)
+    pw = params()
+    pw.sliding_window = 32
+    assert _fwd_call(L, pw, info) == E
+    # the extended entry point wants its options and a known cache format
+    P = ctypes.c_void_p
+    assert L.pa_varlen_fwd_ex(ctypes.byref(p), ctypes.byref(info), P(0x1000), P(0x2000), P(0x3000),
+                              P(0x4000), P(0x5000), P(0x6000), None, info.num_tokens, P(0x7000),
+                              P(0x8000), P(0x10000), 1 << 30, None) == E
+    bad = ops.FwdOptions(7, None, None, None)
+    assert L.pa_varlen_fwd_ex(ctypes.byref(p), ctypes.byref(info), P(0x1000), P(0x2000), P(0x3000),
+                              P(0x4000), P(0x5000), P(0x6000), ctypes.byref(bad), info.num_tokens,
+                              P(0x7000), P(0x8000), P(0x10000), 1 << 30, None) == E
