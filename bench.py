@@ -58,7 +58,7 @@ def parse():
 class Step:
     """Everything one step needs, resident on the GPU."""
 
-    def __init__(self, wl, dev, fp8=False, single_pass=False):
+    def __init__(self, wl, dev, fp8=False, single_pass=False, window=0, sinks=False):
         import torch
         from paged_kv_varlen_flash_amd import ops, workloads as W
         self.ops, self.wl, self.fp8 = ops, wl, fp8
@@ -73,7 +73,12 @@ class Step:
             d["k_scale"] = torch.from_numpy(self.k_scale).to(dev)
             d["v_scale"] = torch.from_numpy(self.v_scale).to(dev)
         self.params = ops.make_params(wl.B, wl.H, wl.Hkv, wl.D, wl.BS, wl.num_blocks,
-                                      wl.block_table.shape[1], wl.causal, wl.scale)
+                                      wl.block_table.shape[1], wl.causal, wl.scale,
+                                      sliding_window=window)
+        self.s_aux = None
+        if sinks:
+            rng = np.random.default_rng(4002)
+            self.s_aux = torch.from_numpy((rng.standard_normal(wl.H) * 2).astype(np.float32)).to(dev)
         self.cu = np.ascontiguousarray(wl.cu_seqlens_q, np.int32)
         self.sk = np.ascontiguousarray(wl.k_lens, np.int32)
         words, info = ops.pa_plan_varlen(self.params, self.cu, self.sk)
@@ -131,7 +136,13 @@ class Step:
 
     def attention(self):
         d, ops = self.d, self.ops
-        if self.fp8:
+        if self.s_aux is not None:
+            ops.pa_varlen_fwd_ex(self.params, self.info, self.worklist, d["q"], d["kv_cache"],
+                                 d["cu_seqlens_q"], d["seqused_k"], d["block_table"], self.out,
+                                 self.lse, self.workspace, None,
+                                 d.get("k_scale") if self.fp8 else None,
+                                 d.get("v_scale") if self.fp8 else None, self.s_aux)
+        elif self.fp8:
             ops.pa_varlen_fwd_fp8(self.params, self.info, self.worklist, d["q"], d["kv_cache"],
                                   d["cu_seqlens_q"], d["seqused_k"], d["block_table"],
                                   d["k_scale"], d["v_scale"], self.out, self.lse, self.workspace)
@@ -253,17 +264,22 @@ def cpu_baseline(wl, budget_s, fp8_step=None):
 _WORKLOADS = {}
 
 
-def measure(name, args, dev, flush, with_cpu, fp8=False, single_pass=False):
+def measure(name, args, dev, flush, with_cpu, fp8=False, single_pass=False, window=0,
+            sinks=False):
     import torch
     from paged_kv_varlen_flash_amd import workloads as W
     if name not in _WORKLOADS:
         print(f"bench: building workload {name}", file=sys.stderr, flush=True)
         _WORKLOADS[name] = W.make(name)
     wl = _WORKLOADS[name]
-    step = Step(wl, dev, fp8, single_pass)
+    step = Step(wl, dev, fp8, single_pass, window, sinks)
     per_step = time_steps(step, args.steps, args.warmup)
     t_mean, t_med = time_attention(step, args.kernel_reps, flush)
     kv = wl.kv_read_bytes() // (2 if fp8 else 1)
+    if window:
+        # keys inside the window only (decode rows: the last W keys)
+        kv = int(2 * np.minimum(wl.k_lens.astype(np.int64), window).sum() * wl.Hkv * wl.D
+                 * (1 if fp8 else 2))
     flops = wl.attention_flops()
     res = {"workload": name, "wl": wl, "ms_per_step": per_step * 1e3, "attn_mean_s": t_mean,
            "attn_median_s": t_med, "kv_bytes": kv, "flops": flops, "plan": step.info.as_dict()}
@@ -377,6 +393,13 @@ def main():
             sec[spec.name] = {"attn_avg_us": round(casc["attn_mean_s"] * 1e6, 2),
                               "single_pass_attn_avg_us": round(one["attn_mean_s"] * 1e6, 2),
                               "cascade_decision": {"common_prefix_len": P, "use_cascade": use}}
+        if not fp8:
+            # decode with a 1024-key sliding window and per-head sinks
+            r = measure("decode_llama8b", args, dev, flush, False, window=1024, sinks=True)
+            sec["decode_llama8b_window1024_sinks"] = {
+                "attn_avg_us": round(r["attn_mean_s"] * 1e6, 2),
+                "kv_GBps": round(r["kv_bytes"] / r["attn_mean_s"] / 1e9, 1),
+                "hbm_frac": round(r["kv_bytes"] / r["attn_mean_s"] / 1e9 / HBM_PEAK_GBS, 4)}
         if not fp8:
             r = measure("decode_llama8b", args, dev, flush, False, fp8=True)
             sec["decode_llama8b_fp8"] = {
