@@ -45,7 +45,9 @@ typedef enum {
 /* Static string naming a status code. */
 const char* pa_status_str(pa_status s);
 
-/* Library version, (major << 16) | minor. */
+/* Library version, (major << 16) | minor.  Major 2: pa_attn_params and
+ * pa_plan_info carry sliding_window, reduce items carry the sequence's first
+ * token (work-list version 2). */
 int32_t pa_version(void);
 
 /* Head sizes with a compiled kernel. */
@@ -366,7 +368,7 @@ pa_status pa_merge_attn_states(void* out, float* out_lse,
  * A "row" of sequence b is (query token i, head-in-group g) -> row i*G + g,
  * G = H / Hkv; kv_head's query heads are kv_head*G .. kv_head*G + G-1.    */
 #define PA_WORKLIST_MAGIC 0x50414731
-#define PA_WORKLIST_VERSION 1
+#define PA_WORKLIST_VERSION 2
 #define PA_WORKLIST_HEADER_WORDS 16
 #define PA_ITEM_WORDS 8
 #define PA_SMALL_MAX_ROWS 16

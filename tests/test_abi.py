@@ -43,7 +43,7 @@ def test_status_strings_and_version(L):
     assert ops.status_str(0) == "PA_OK"
     assert ops.status_str(3) == "PA_ERR_WORKSPACE_TOO_SMALL"
     assert ops.status_str(99) == "PA_ERR_UNKNOWN"
-    assert L.pa_version() >> 16 == 1
+    assert L.pa_version() >> 16 == 2
     assert ops.supported_head_sizes() == [64, 128, 256]
 
 
@@ -219,7 +219,7 @@ def test_cascade_split(L):
 
 # ---------------------------------------------------------------- plan coverage
 def parse(wl_words, info):
-    assert wl_words[0] == ops.PA_WORKLIST_MAGIC
+    assert wl_words[0] == ops.PA_WORKLIST_MAGIC and wl_words[1] == 2
     n_att = info.num_small_items + info.num_tiled_items
     items = wl_words[16:16 + 8 * n_att].reshape(-1, 8)
     red = wl_words[16 + 8 * n_att:].reshape(-1, 8)
