@@ -359,18 +359,21 @@ pa_status pa_merge_attn_states(void* out, float* out_lse,
  * items, PA_ITEM_WORDS words each.
  * attention item: seq, kv_head, row0, nrows, kv_begin, kv_end,
  *   partial_row (-1: write out/lse directly), kind (0: small-row item of
- *   <= PA_SMALL_MAX_ROWS rows, 1: tiled item of <= PA_TILED_ROWS rows).
+ *   <= PA_SMALL_MAX_ROWS rows, 1: tiled item of <= PA_TILED_ROWS rows),
+ *   first token of the sequence (cu_seqlens_q[seq]), Lk - Lq of the
+ *   sequence, 0, 0.  Rows and key range are clipped to the sequence, so the
+ *   kernels read no lengths from device memory.
  *   When both kinds are present they are interleaved, longest estimated
  *   time first, and run as one launch; otherwise all items are one kind.
  * reduce item: seq, kv_head, row0, nrows, partial_row0, num_splits,
- *   first token of the sequence (cu_seqlens_q[seq]), 0
+ *   first token of the sequence (cu_seqlens_q[seq]), 0, 0, 0, 0, 0
  *   (split s of the unit wrote rows partial_row0 + s * nrows ...)
  * A "row" of sequence b is (query token i, head-in-group g) -> row i*G + g,
  * G = H / Hkv; kv_head's query heads are kv_head*G .. kv_head*G + G-1.    */
 #define PA_WORKLIST_MAGIC 0x50414731
 #define PA_WORKLIST_VERSION 2
 #define PA_WORKLIST_HEADER_WORDS 16
-#define PA_ITEM_WORDS 8
+#define PA_ITEM_WORDS 12
 #define PA_SMALL_MAX_ROWS 16
 #define PA_TILED_ROWS 128
 

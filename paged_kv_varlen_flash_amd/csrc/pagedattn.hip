@@ -148,6 +148,8 @@ __device__ __forceinline__ float ld_uniform(const float* p) {
 
 struct Item {
   int seq, kvh, row0, nrows, kv0, kv1, prow;
+  int t0;     // the sequence's first query token
+  int koff;   // Lk - Lq: query i's last visible key under the causal mask is i + koff
 };
 
 __device__ __forceinline__ Item load_item(const int32_t* p) {
@@ -159,6 +161,8 @@ __device__ __forceinline__ Item load_item(const int32_t* p) {
   it.kv0 = ld_uniform(p + 4);
   it.kv1 = ld_uniform(p + 5);
   it.prow = ld_uniform(p + 6);
+  it.t0 = ld_uniform(p + 8);
+  it.koff = ld_uniform(p + 9);
   return it;
 }
 
@@ -320,20 +324,20 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int n = lane & 15, g = lane >> 4;
   const Item it = load_item(item);
-  const int t0 = ld_uniform(a.cu + it.seq);
-  const int Lq = ld_uniform(a.cu + it.seq + 1) - t0;
-  const int Lk = ld_uniform(a.seqused_k + it.seq);
+  // the item carries the sequence's first token and causal offset, and its
+  // rows and key range are already clipped to the sequence
+  const int t0 = it.t0;
   const int G = a.G;
-  const int nrows = min(it.nrows, Lq * G - it.row0);
-  const int kv1 = min(min(it.kv1, Lk), a.MB * a.BS);
+  const int nrows = it.nrows;
+  const int kv1 = min(it.kv1, a.MB * a.BS);
   const int kv0 = it.kv0;
 
   const int r = it.row0 + n;
   const bool row_ok = n < nrows;
   const int tok = r / G;
   const int head = it.kvh * G + (r - tok * G);
-  const int row_limit = a.causal ? tok + Lk - Lq : INT_MAX;
-  const int row_lo = a.window > 0 ? tok + Lk - Lq - (a.window - 1) : INT_MIN;
+  const int row_limit = a.causal ? tok + it.koff : INT_MAX;
+  const int row_lo = a.window > 0 ? tok + it.koff - (a.window - 1) : INT_MIN;
   // an E4M3 cache holds K / k_scale and V / v_scale of each KV head: the
   // scores take k_scale inside the exponent's factor, O takes v_scale at the end
   const float sl2 = FP8 ? a.scale_log2 * ld_uniform(a.k_scale + it.kvh) : a.scale_log2;
@@ -605,28 +609,28 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
   const Item it = load_item(item);
-  const int t0 = ld_uniform(a.cu + it.seq);
-  const int Lq = ld_uniform(a.cu + it.seq + 1) - t0;
-  const int Lk = ld_uniform(a.seqused_k + it.seq);
+  // the item carries the sequence's first token and causal offset, and its
+  // rows and key range are already clipped to the sequence
+  const int t0 = it.t0;
   const int G = a.G;
-  const int nrows = min(it.nrows, Lq * G - it.row0);
-  const int kv1 = min(min(it.kv1, Lk), a.MB * a.BS);
+  const int nrows = it.nrows;
+  const int kv1 = min(it.kv1, a.MB * a.BS);
 
   const int rl = wave * 32 + n;
   const int r = it.row0 + rl;
   const bool row_ok = rl < nrows;
   const int tok = r / G;
   const int head = it.kvh * G + (r - tok * G);
-  const int row_limit = a.causal ? tok + Lk - Lq : INT_MAX;
+  const int row_limit = a.causal ? tok + it.koff : INT_MAX;
   // an E4M3 cache holds K / k_scale and V / v_scale of each KV head: the
   // scores take k_scale inside the exponent's factor, O takes v_scale at the end
   const float sl2 = FP8 ? a.scale_log2 * ld_uniform(a.k_scale + it.kvh) : a.scale_log2;
   const float vsc = FP8 ? ld_uniform(a.v_scale + it.kvh) : 1.f;
   // every row of this wave sees keys up to at least wave_limit, and (with a
   // sliding window) no row of it sees a key below wave_lo
-  const int wave_limit = a.causal ? (it.row0 + wave * 32) / G + Lk - Lq : INT_MAX;
-  const int wave_lo = a.window > 0 ? (it.row0 + wave * 32 + 31) / G + Lk - Lq - (a.window - 1) : INT_MIN;
-  const int row_lo = a.window > 0 ? tok + Lk - Lq - (a.window - 1) : INT_MIN;
+  const int wave_limit = a.causal ? (it.row0 + wave * 32) / G + it.koff : INT_MAX;
+  const int wave_lo = a.window > 0 ? (it.row0 + wave * 32 + 31) / G + it.koff - (a.window - 1) : INT_MIN;
+  const int row_lo = a.window > 0 ? tok + it.koff - (a.window - 1) : INT_MIN;
 
   bf16x8_t qf[NKT];
   if (row_ok) {

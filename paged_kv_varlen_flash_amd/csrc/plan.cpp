@@ -173,6 +173,8 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
   tiled_items.clear();
   reduce_items.clear();
   int64_t prow = 0;
+  // Lk - Lq of a unit's sequence
+  auto koff = [&](const Unit& u) { return sk[u.seq] - (cu[u.seq + 1] - cu[u.seq]); };
   // a unit whose range became items [first, end) of `dst`: when it is split,
   // give every piece its partial rows and add the reduce item
   auto finish_unit = [&](const Unit& u, std::vector<Item>& dst, size_t first) -> bool {
@@ -180,7 +182,7 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
     if (n <= 1) return true;
     for (int64_t s = 0; s < n; ++s) dst[first + s].w[6] = (int32_t)(prow + s * u.nrows);
     reduce_items.push_back(
-        Item{{u.seq, u.kvh, u.row0, u.nrows, (int32_t)prow, (int32_t)n, cu[u.seq], 0}, 0});
+        Item{{u.seq, u.kvh, u.row0, u.nrows, (int32_t)prow, (int32_t)n, cu[u.seq], 0, 0, 0, 0, 0}, 0});
     prow += n * u.nrows;
     return prow <= INT32_MAX / 2;
   };
@@ -213,7 +215,8 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
         // tiled items' (a small-row workgroup streams a key about as fast as
         // a full 128-row tiled one computes it)
         small_items.push_back(
-            Item{{u.seq, u.kvh, u.row0, u.nrows, k0, k1, -1, 0}, (int64_t)(k1 - k0) * PA_TILED_ROWS});
+            Item{{u.seq, u.kvh, u.row0, u.nrows, k0, k1, -1, 0, cu[u.seq], koff(u), 0, 0},
+                 (int64_t)(k1 - k0) * PA_TILED_ROWS});
         k0 = k1;
       } while (k0 < u.kv_end);
       if (!finish_unit(u, small_items, first)) return PA_ERR_INVALID_ARGUMENT;
@@ -245,7 +248,8 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
     do {
       const int32_t k1 = std::min(u.kv_end, k0 + chunk);
       tiled_items.push_back(
-          Item{{u.seq, u.kvh, u.row0, u.nrows, k0, k1, -1, 1}, (int64_t)(k1 - k0) * u.nrows});
+          Item{{u.seq, u.kvh, u.row0, u.nrows, k0, k1, -1, 1, cu[u.seq], koff(u), 0, 0},
+               (int64_t)(k1 - k0) * u.nrows});
       k0 = k1;
     } while (k0 < u.kv_end);
     if (!finish_unit(u, tiled_items, first)) return PA_ERR_INVALID_ARGUMENT;

@@ -29,7 +29,7 @@ PA_ERR_WORKSPACE_TOO_SMALL = 3
 PA_ERR_HIP = 4
 PA_WORKLIST_MAGIC = 0x50414731
 PA_WORKLIST_HEADER_WORDS = 16
-PA_ITEM_WORDS = 8
+PA_ITEM_WORDS = 12
 PLAN_TARGET_CUS = 256          # compute units the planner schedules for (PA_PLAN_TARGET_CUS)
 
 EXPORTED = ["pa_status_str", "pa_version", "pa_supported_head_sizes", "pa_plan_varlen",

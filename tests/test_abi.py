@@ -221,8 +221,9 @@ def test_cascade_split(L):
 def parse(wl_words, info):
     assert wl_words[0] == ops.PA_WORKLIST_MAGIC and wl_words[1] == 2
     n_att = info.num_small_items + info.num_tiled_items
-    items = wl_words[16:16 + 8 * n_att].reshape(-1, 8)
-    red = wl_words[16 + 8 * n_att:].reshape(-1, 8)
+    IW = ops.PA_ITEM_WORDS
+    items = wl_words[16:16 + IW * n_att].reshape(-1, IW)
+    red = wl_words[16 + IW * n_att:].reshape(-1, IW)
     assert len(red) == info.num_reduce_items
     return items, red
 
@@ -241,7 +242,10 @@ def check_plan_covers(H, Hkv, q_lens, k_lens, causal, force_splits=0):
     small_rows = PA_SMALL = 16
     assert (items[:, 7] == 0).sum() == info.num_small_items
     assert (items[:, 7] == 1).sum() == info.num_tiled_items
-    for idx, (seq, kvh, row0, nrows, k0, k1, prow, kind) in enumerate(items):
+    # words 8, 9: the sequence's first token and Lk - Lq
+    assert np.array_equal(items[:, 8], cu[items[:, 0]])
+    assert np.array_equal(items[:, 9], np.asarray(k_lens)[items[:, 0]] - np.diff(cu)[items[:, 0]])
+    for idx, (seq, kvh, row0, nrows, k0, k1, prow, kind, *_) in enumerate(items):
         is_small = kind == 0
         assert nrows <= (PA_SMALL if is_small else 128) and nrows >= 1
         for r in range(row0, row0 + nrows):
@@ -268,7 +272,7 @@ def check_plan_covers(H, Hkv, q_lens, k_lens, causal, force_splits=0):
                     assert ranges[0][2] == -1
     assert not cover, "items for rows that do not exist"
     # reduce items point at the split items' partial rows
-    for seq, kvh, row0, nrows, prow0, nsplit, tok0, _ in red:
+    for seq, kvh, row0, nrows, prow0, nsplit, tok0, *_ in red:
         assert nsplit >= 2
         assert tok0 == cu[seq]                       # first token of the sequence
         assert row0 + nrows <= q_lens[seq] * G       # rows are clipped by the planner
@@ -328,7 +332,7 @@ def test_small_items_longest_first(L):
     cost = (small[:, 5] - small[:, 4]) * small[:, 3]
     assert np.all(np.diff(cost) <= 0)
     assert (small[:, 5] - small[:, 4]).sum() == int(wl.k_lens.sum()) * wl.Hkv
-    for seq, kvh, row0, nrows, k0, k1, prow, _ in small:
+    for seq, kvh, row0, nrows, k0, k1, prow, *_ in small:
         if prow >= 0 and k1 != wl.k_lens[seq]:
             assert (k1 - k0) % 64 == 0 and k0 % 64 == 0
 
@@ -441,7 +445,7 @@ def test_plan_covers_sliding_window(L, seed):
     assert info.sliding_window == W_
     items, red = parse(words, info)
     cover = {}
-    for seq, kvh, row0, nrows, k0, k1, prow, word7 in items:
+    for seq, kvh, row0, nrows, k0, k1, prow, word7, *_ in items:
         assert k0 % 16 == 0
         for r in range(row0, row0 + nrows):
             cover.setdefault((seq, kvh, r), []).append((k0, k1))
