@@ -165,6 +165,29 @@ def test_fuzz(seed):
     _check_case(spec, rng, force, f"fuzz{seed}")
 
 
+# Scores spread over hundreds of natural-log units: a row maximum taken over
+# only part of a row's keys (a wrong cross-lane exchange) overflows exp2, and
+# a wrong reference shifts the LSE.  Decode rows (small-row kernel: maxima
+# across 16- and 32-lane groups) and prefill rows (tiled kernel).
+EXTREME = [
+    # D, G, Hkv, BS, causal, (Lq, Lk) per sequence, q multiplier, scale multiplier
+    (128, 4, 2, 16, True, ((1, 700), (1, 40), (2, 300)), 8.0, 4.0),
+    (128, 4, 2, 32, True, ((100, 100), (40, 500)), 8.0, 4.0),
+    (64, 8, 1, 16, False, ((1, 200), (60, 90)), 6.0, 6.0),
+    (256, 8, 2, 64, True, ((1, 1000), (30, 200)), 6.0, 3.0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(EXTREME)))
+def test_extreme_scores(case):
+    D, G, Hkv, BS, causal, seqs, qmul, smul = EXTREME[case]
+    spec = W.Spec(name=f"extreme{case}", num_heads=G * Hkv, num_kv_heads=Hkv, head_size=D,
+                  block_size=BS, causal=causal, seed=7300 + case, fixed=seqs, min_num_blocks=3)
+    say(f"extreme scores case={case} D={D} G={G} seqs={seqs} q x{qmul} scale x{smul}")
+    _check_case(spec, np.random.default_rng(7300 + case), 0, f"extreme{case}", qmul=qmul,
+                smul=smul)
+
+
 # Batches whose every sequence has more than 16 rows (query tokens x heads
 # per KV head), so that the launch holds tiled items only: ragged tails,
 # rows that see no key (Lq > Lk under the causal mask), split key ranges.
@@ -190,7 +213,7 @@ def test_prefill_only(case):
     assert plan.info.num_small_items == 0 and plan.info.num_tiled_items > 0
 
 
-def _check_case(spec, rng, force, label):
+def _check_case(spec, rng, force, label, qmul=1.0, smul=1.0):
     q_lens = np.array([a for a, _ in spec.fixed], np.int32)
     k_lens = np.array([b for _, b in spec.fixed], np.int32)
     B, H, Hkv, D, BS = len(q_lens), spec.num_heads, spec.num_kv_heads, spec.head_size, spec.block_size
@@ -206,12 +229,14 @@ def _check_case(spec, rng, force, label):
     cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
     T = int(cu[-1])
     q = W.randn_bf16(rng, (T, H, D))
+    if qmul != 1.0:                        # exact: a power of two times bf16, or rounded again
+        q = W.f32_to_bf16_bits((q.astype(np.uint32) << 16).view(np.float32) * np.float32(qmul))
     cache = W.randn_bf16(rng, (2, NB, BS, Hkv, D))
     # slack slots hold NaN: they must never reach an output
     for b in range(B):
         for j in range(k_lens[b], nblk[b] * BS):
             cache[:, bt[b, j // BS], j % BS] = W.SENTINEL
-    scale = np.float32(1.0 / np.sqrt(D))
+    scale = np.float32(smul / np.sqrt(D))
     p = ops.make_params(B, H, Hkv, D, BS, NB, MB, spec.causal, scale)
     plan = ops.VarlenPlan(p, cu, k_lens, force)
     tq = torch.from_numpy(q.view(np.int16)).cuda().view(torch.bfloat16)
