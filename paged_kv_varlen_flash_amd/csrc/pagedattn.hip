@@ -281,7 +281,13 @@ struct SmallCfg {
   static constexpr int CPR = D / 8;          // 16-byte chunks per key row
   static constexpr int LPR = 64 / CPR;       // key rows per wave load instruction
   static constexpr int NLD = 16 / LPR;       // load instructions per plane per step
-  static constexpr int PF = (D == 256) ? 2 : 3;  // steps of loads in flight
+  // steps of loads in flight per wave at 2 waves per SIMD (the mixed
+  // kernel); the small-row kernel runs D = 128 with two steps, which fits
+  // the registers of 3 waves per SIMD (4 with an E4M3 cache): as many bytes
+  // in flight per compute unit, and a third (fourth) workgroup covers
+  // another's start-up
+  static constexpr int PF = (D == 256) ? 2 : 3;
+  static constexpr int PF_SMALL = (D >= 128) ? 2 : 3;
   static constexpr int RB = D * 2;           // bytes per LDS row
   static constexpr int WAVE_LDS = 2 * 16 * RB;
 };
@@ -310,11 +316,11 @@ struct SmallLoad {
   static constexpr int NLD = 16 / LPR;       // load instructions per plane per step
 };
 
-template <int D, bool FP8>
+template <int D, bool FP8, int PF>
 __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* item, uint8_t* smem) {
   using C = SmallCfg<D>;
   using LD = SmallLoad<D, FP8>;
-  constexpr int CPR = C::CPR, PF = C::PF, RB = C::RB;
+  constexpr int CPR = C::CPR, RB = C::RB;
   constexpr int LPR = LD::LPR, NLD = LD::NLD, ES = LD::ES;
   constexpr int NT = D / 32;        // QK k-steps
   constexpr int NDT = D / 16;       // 16-wide d tiles of O^T
@@ -553,9 +559,9 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
 }
 
 template <int D, bool FP8>
-__global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, (D <= 128 ? (FP8 ? 4 : 3) : 1)) void attn_small_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[small_lds_bytes<D>()];
-  small_body<D, FP8>(a, a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS, smem);
+  small_body<D, FP8, SmallCfg<D>::PF_SMALL>(a, a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -944,7 +950,7 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_mixed_kernel(Att
   if (ld_uniform(item + 7))
     tiled_body<D, FP8>(a, item, smem);
   else
-    small_body<D, FP8>(a, item, smem);
+    small_body<D, FP8, SmallCfg<D>::PF>(a, item, smem);
 }
 
 // ---------------------------------------------------------------------------
