@@ -194,7 +194,8 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
   if (n_small > 0) {
     const int64_t chunk = std::max<int64_t>(
         kSmallMinChunk,
-        ceil_div(ceil_div(std::max<int64_t>(small_keys, 1), target * kSmallItemsPerCu), 64) * 64);
+        ceil_div(ceil_div(std::max<int64_t>(small_keys, 1),
+                          (int64_t)(target * kSmallItemsPerCu)), 64) * 64);
     for (const Unit& u : units) {
       if (!u.small) continue;
       const size_t first = small_items.size();
