@@ -656,30 +656,37 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
   const int bs_log2 = a.bs_log2;
 
   bf16x8_t kr[LOADS], vr[LOADS];
+  // buffer-load geometry: bytes between key rows of one head, and this
+  // thread's byte offset from the first key row of a pass (the same for
+  // every pass and tile)
+  const int row_bytes = (int)(row_elems * 2);
+  const int ld_off = lkey * row_bytes + lcol * 16;
+  const uint8_t* cache_b = reinterpret_cast<const uint8_t*>(a.cache) + (int64_t)it.kvh * D * 2;
   auto load_tile = [&](int j0) {
     if constexpr (KSTEP <= 16) {
       // tiles start on a multiple of 16 and blocks hold a multiple of 16
-      // keys, so the KSTEP keys of pass i share one block: the lookups are
-      // wave-uniform, done as scalar loads outside the per-lane tail branch
-      int phys[LOADS], base[LOADS];
+      // keys, so the KSTEP keys of pass i share one block: the lookup is a
+      // wave-uniform scalar load, and the pass is one bounds-checked buffer
+      // load per plane through a resource that starts at the pass's first
+      // key row and ends at the range's last key (rows past it read as
+      // zero, with no per-lane branch or 64-bit address arithmetic)
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        const int kg = min(j0 + KSTEP * i, kv1 - 1);
-        const int blk = (bs_log2 >= 0) ? (kg >> bs_log2) : (kg / a.BS);
-        base[i] = (j0 + KSTEP * i) - blk * a.BS;
-        phys[i] = ld_uniform(btrow + blk);
-      }
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int key = j0 + lkey + KSTEP * i;
-        if (key < kv1) {
-          const uint16_t* p = cbase + ((int64_t)phys[i] * a.BS + base[i] + lkey) * row_elems;
-          kr[i] = ld16(p);
-          vr[i] = ld16(p + a.plane);
-        } else {
-          kr[i] = zero8();
-          vr[i] = zero8();
+        const int kb = j0 + KSTEP * i;
+        int nrec = 0;
+        int64_t boff = 0;
+        if (kb < kv1) {
+          const int blk = (bs_log2 >= 0) ? (kb >> bs_log2) : (kb / a.BS);
+          const int phys = ld_uniform(btrow + blk);
+          boff = ((int64_t)phys * a.BS + (kb - blk * a.BS)) * row_elems * 2;
+          nrec = (min(KSTEP, kv1 - kb) - 1) * row_bytes + D * 2;
         }
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(cache_b + boff), 0, nrec, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(cache_b + a.plane * 2 + boff), 0, nrec, 0x00020000);
+        kr[i] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rk, ld_off, 0, 0));
+        vr[i] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rv, ld_off, 0, 0));
       }
     } else {
 #pragma unroll
