@@ -89,6 +89,11 @@ SPECS = {
         groups=(("prefill", 8, 256, 2048), ("decode", 56, 256, 4096)), shuffle_order=True,
         description="8 causal prefills L~U[256,2048] + 56 decodes Lk~U[256,4096]; "
                     "H=32 Hkv=8 D=128 BS=32, one launch"),
+    "chunked_prefill_mix_prefill": Spec(
+        name="chunked_prefill_mix_prefill", num_heads=32, num_kv_heads=8, head_size=128,
+        block_size=32, causal=True, seed=1003, groups=(("prefill", 8, 256, 2048),),
+        description="the 8 causal prefills of chunked_prefill_mix alone (the same seed draws "
+                    "the same lengths first); H=32 Hkv=8 D=128 BS=32"),
     "cascade_prefix": Spec(
         name="cascade_prefix", num_heads=32, num_kv_heads=8, head_size=128, block_size=16,
         causal=True, seed=1004, groups=(("decode", 32, 64, 512),), shared_prefix=2048,

@@ -75,3 +75,14 @@ def test_regenerate_one_sequence():
         nb = (wl.k_lens[b] + 15) // 16
         ids = wl.block_table[b, :nb]
         assert np.array_equal(wl.kv_cache[:, ids], full.kv_cache[:, ids])
+
+
+def test_prefill_rows_of_the_mix():
+    """chunked_prefill_mix_prefill holds exactly the prefill sequences of
+    chunked_prefill_mix (same lengths, no decodes)."""
+    mix = W.make("chunked_prefill_mix", materialise=False)
+    pre = W.make("chunked_prefill_mix_prefill", materialise=False)
+    rows = mix.q_lens > 1
+    assert np.array_equal(np.sort(mix.q_lens[rows]), np.sort(pre.q_lens))
+    assert np.array_equal(np.sort(mix.k_lens[rows]), np.sort(pre.k_lens))
+    assert np.array_equal(pre.q_lens, pre.k_lens) and pre.q_lens.size == 8
