@@ -290,6 +290,9 @@ struct SmallCfg {
   static constexpr int PF_SMALL = (D >= 128) ? 2 : 3;
   static constexpr int RB = D * 2;           // bytes per LDS row
   static constexpr int WAVE_LDS = 2 * 16 * RB;
+  // floats per row of the epilogue's merge area: the 4-float pad puts the
+  // 16 rows of a 16-byte store or load in different banks
+  static constexpr int SD = D + 4;
 };
 
 // chunk position of (row r, chunk c) inside an LDS row
@@ -302,8 +305,9 @@ __device__ __forceinline__ int swz(int r, int c) {
 // merge area
 template <int D>
 constexpr int small_lds_bytes() {
-  return (4 * SmallCfg<D>::WAVE_LDS > (4 * 16 * D + 3 * 64) * 4) ? 4 * SmallCfg<D>::WAVE_LDS
-                                                                  : (4 * 16 * D + 3 * 64) * 4;
+  return (4 * SmallCfg<D>::WAVE_LDS > (4 * 16 * SmallCfg<D>::SD + 3 * 64) * 4)
+             ? 4 * SmallCfg<D>::WAVE_LDS
+             : (4 * 16 * SmallCfg<D>::SD + 3 * 64) * 4;
 }
 
 // loads of one key row: D*ES bytes in 16-byte chunks (ES = 1 for an E4M3
@@ -490,14 +494,14 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
   lr_run += __shfl_xor(lr_run, 16);
   lr_run += __shfl_xor(lr_run, 32);
   __syncthreads();
+  constexpr int SD = C::SD;
   float* so = reinterpret_cast<float*>(smem);
-  float* sm = so + 4 * 16 * D;
+  float* sm = so + 4 * 16 * SD;
   float* sl = sm + 64;
   float* sr = sl + 64;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) so[(wave * 16 + n) * D + 16 * dt + 4 * g + i] = o[dt][i];
+    *reinterpret_cast<f32x4_t*>(so + (wave * 16 + n) * SD + 16 * dt + 4 * g) = o[dt];
   if (g == 0) {
     sm[wave * 16 + n] = m_run;
     sl[wave * 16 + n] = l_run;
@@ -528,11 +532,13 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
     const float lse_v = empty ? kNegInf : (M + __log2f(L)) * kLn2;
     float acc[DPT];
 #pragma unroll
-    for (int e = 0; e < DPT; ++e) {
-      float sum = 0.f;
+    for (int e = 0; e < DPT; e += 4) {
+      f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w = 0; w < 4; ++w) sum += wt[w] * so[(w * 16 + er) * D + ec * DPT + e];
-      acc[e] = sum * inv;
+      for (int w = 0; w < 4; ++w)
+        sum += wt[w] * *reinterpret_cast<const f32x4_t*>(so + (w * 16 + er) * SD + ec * DPT + e);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[e + k] = sum[k] * inv;
     }
     if (it.prow < 0) {
       const int64_t orow = (int64_t)(t0 + etok) * a.H + ehead;
