@@ -132,6 +132,40 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask));
 }
 
+// The values of lanes l and l ^ 16 (v_permlane16_swap) or l and l ^ 32
+// (v_permlane32_swap), in lane order: a VALU exchange with no LDS traffic
+// or wait.  max and a two-term sum of the pair equal those of l and its
+// partner exactly.
+template <int X>
+__device__ __forceinline__ void lane_pair(float v, float& a, float& b) {
+  static_assert(X == 16 || X == 32, "lane_pair");
+  const uint32_t w = __builtin_bit_cast(uint32_t, v);
+  uint32_t r0, r1;
+  if constexpr (X == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+    r0 = r[0];
+    r1 = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    r0 = r[0];
+    r1 = r[1];
+  }
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+template <int X>
+__device__ __forceinline__ float max_xor(float v) {
+  float a, b;
+  lane_pair<X>(v, a, b);
+  return fmaxf(a, b);
+}
+template <int X>
+__device__ __forceinline__ float sum_xor(float v) {
+  float a, b;
+  lane_pair<X>(v, a, b);
+  return a + b;
+}
+
 // Load of a wave-uniform int32 from memory that no kernel of the launch
 // writes (work list, lengths, block table): through the constant address
 // space, so it becomes a scalar load instead of a vector load whose wait
@@ -456,8 +490,8 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
         x[i] = (key >= kv1 || key > row_limit || key < row_lo) ? kNegInf : s[i] * sl2;
       }
       float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      mx = wave_max_xor(mx, 16);
-      mx = wave_max_xor(mx, 32);
+      mx = max_xor<16>(mx);
+      mx = max_xor<32>(mx);
       const float m_new = fmaxf(m_run, mx);
       const float m_use = (m_new == kNegInf) ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
@@ -489,10 +523,8 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
   }
 
   // ---- merge the four waves' partial states through LDS
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  lr_run += __shfl_xor(lr_run, 16);
-  lr_run += __shfl_xor(lr_run, 32);
+  l_run = sum_xor<32>(sum_xor<16>(l_run));
+  lr_run = sum_xor<32>(sum_xor<16>(lr_run));
   __syncthreads();
   constexpr int SD = C::SD;
   float* so = reinterpret_cast<float*>(smem);
