@@ -128,10 +128,6 @@ __device__ __forceinline__ bf16x8_t cat(bf16x4_t a, bf16x4_t b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-__device__ __forceinline__ float wave_max_xor(float v, int mask) {
-  return fmaxf(v, __shfl_xor(v, mask));
-}
-
 // The values of lanes l and l ^ 16 (v_permlane16_swap) or l and l ^ 32
 // (v_permlane32_swap), in lane order: a VALU exchange with no LDS traffic
 // or wait.  max and a two-term sum of the pair equal those of l and its
@@ -901,7 +897,7 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
     float mx = x[0];
 #pragma unroll
     for (int i = 1; i < 32; ++i) mx = fmaxf(mx, x[i]);
-    mx = wave_max_xor(mx, 32) * sl2;
+    mx = max_xor<32>(mx) * sl2;
     if (__builtin_expect(__any(mx > m_run + kRescaleSlack), 0)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -1001,8 +997,8 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
     __syncthreads();
   }
 
-  l_run += __shfl_xor(l_run, 32);
-  lr_run += __shfl_xor(lr_run, 32);
+  l_run = sum_xor<32>(l_run);
+  lr_run = sum_xor<32>(lr_run);
   if (!row_ok) return;
   float fo = 1.f;      // rescales O when a sink moves the reference
   if (a.s_aux && it.prow < 0) fo = add_sink(a.s_aux[head] * kLog2e, m_run, l_run, lr_run);
