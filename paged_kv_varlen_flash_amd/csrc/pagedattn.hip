@@ -399,6 +399,16 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
   const int64_t row_elems = (int64_t)a.Hkv * D;
   const int32_t* btrow = a.block_table + (int64_t)it.seq * a.bt_stride;
   uint8_t* wl = smem + wave * C::WAVE_LDS;       // K rows [0,16), V rows [16,32)
+  // chunk position in LDS.  An E4M3 lane widens one 16-byte code chunk into
+  // bf16 chunks 2c and 2c+1 and stores them with two instructions, and 8
+  // lanes (one key row at D >= 128) share an LDS pass of 128 bytes: with the
+  // two halves of code chunks 4..7 of every 8 trading places, each pass of
+  // each store covers the 8 bank groups once (measured: 4.5 M conflict
+  // cycles per launch without).  Readers see a uniform permutation of the
+  // chunks they read.
+  auto sw = [](int r, int c) {
+    return swz<CPR>(r, (FP8 && D >= 128) ? (c ^ ((c >> 3) & 1)) : c);
+  };
 
   const int nsteps = (kv1 > kv0 + wave * 16) ? (kv1 - kv0 - wave * 16 + 63) / 64 : 0;
 
@@ -459,13 +469,13 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
           u32x4_t k0, k1, v0, v1;
           e4m3x16_to_bf16(buf[p][i], k0, k1);
           e4m3x16_to_bf16(buf[p][NLD + i], v0, v1);
-          *reinterpret_cast<u32x4_t*>(wl + row * RB + swz<CPR>(row, 2 * lc) * 16) = k0;
-          *reinterpret_cast<u32x4_t*>(wl + row * RB + swz<CPR>(row, 2 * lc + 1) * 16) = k1;
-          *reinterpret_cast<u32x4_t*>(wl + (16 + row) * RB + swz<CPR>(row, 2 * lc) * 16) = v0;
-          *reinterpret_cast<u32x4_t*>(wl + (16 + row) * RB + swz<CPR>(row, 2 * lc + 1) * 16) = v1;
+          *reinterpret_cast<u32x4_t*>(wl + row * RB + sw(row, 2 * lc) * 16) = k0;
+          *reinterpret_cast<u32x4_t*>(wl + row * RB + sw(row, 2 * lc + 1) * 16) = k1;
+          *reinterpret_cast<u32x4_t*>(wl + (16 + row) * RB + sw(row, 2 * lc) * 16) = v0;
+          *reinterpret_cast<u32x4_t*>(wl + (16 + row) * RB + sw(row, 2 * lc + 1) * 16) = v1;
         } else {
-          *reinterpret_cast<u32x4_t*>(wl + row * RB + swz<CPR>(row, lc) * 16) = buf[p][i];
-          *reinterpret_cast<u32x4_t*>(wl + (16 + row) * RB + swz<CPR>(row, lc) * 16) = buf[p][NLD + i];
+          *reinterpret_cast<u32x4_t*>(wl + row * RB + sw(row, lc) * 16) = buf[p][i];
+          *reinterpret_cast<u32x4_t*>(wl + (16 + row) * RB + sw(row, lc) * 16) = buf[p][NLD + i];
         }
       }
       issue(buf[p], st + PF);
@@ -476,7 +486,7 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const bf16x8_t ka =
-            *reinterpret_cast<const bf16x8_t*>(wl + n * RB + swz<CPR>(n, 4 * t + g) * 16);
+            *reinterpret_cast<const bf16x8_t*>(wl + n * RB + sw(n, 4 * t + g) * 16);
         s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[t], s, 0, 0, 0);
       }
       float x[4];
@@ -512,7 +522,7 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const int chunk = 2 * dt + ((n & 3) >> 1);
-        const bf16x4_t av = lds_read_tr(reinterpret_cast<const uint16_t*>(vrow + swz<CPR>(vr, chunk) * 16));
+        const bf16x4_t av = lds_read_tr(reinterpret_cast<const uint16_t*>(vrow + sw(vr, chunk) * 16));
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pb, o[dt], 0, 0, 0);
       }
     }
