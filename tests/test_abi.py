@@ -337,6 +337,44 @@ def test_small_items_longest_first(L):
             assert (k1 - k0) % 64 == 0 and k0 % 64 == 0
 
 
+def test_mixed_launch_order(L):
+    """A mixed launch lists each kind longest first, merged in proportion to
+    their counts: after m items the number of tiled items is within one of
+    m * (tiled items / all items)."""
+    wl = W.make("chunked_prefill_mix", materialise=False)
+    p = ops.make_params(wl.B, wl.H, wl.Hkv, wl.D, wl.BS, wl.num_blocks, wl.block_table.shape[1],
+                        True, wl.scale)
+    words, info = ops.pa_plan_varlen(p, wl.cu_seqlens_q, wl.k_lens)
+    items, _ = parse(words, info)
+    tiled = items[:, 7] == 1
+    for kind in (False, True):
+        it = items[tiled == kind]
+        cost = (it[:, 5] - it[:, 4]).astype(np.int64) * (it[:, 3] if kind else 128)
+        assert np.all(np.diff(cost) <= 0)
+    n, nt = len(items), int(tiled.sum())
+    m = np.arange(1, n + 1)
+    assert np.all(np.abs(np.cumsum(tiled) - m * nt / n) <= 1.0)
+
+
+def test_large_plan_order_is_stable(L):
+    """From 2048 items up the planner orders by a radix sort: costs are
+    non-increasing and equal costs keep the units' order (sequence, KV head,
+    first key)."""
+    B, H, Hkv = 600, 32, 8
+    rng = np.random.default_rng(5)
+    k_lens = rng.integers(100, 3000, size=B).astype(np.int32)
+    cu = np.arange(B + 1, dtype=np.int32)
+    p = ops.make_params(B, H, Hkv, 128, 16, 200000, 256, True, 0.1)
+    words, info = ops.pa_plan_varlen(p, cu, k_lens)
+    items, _ = parse(words, info)
+    assert len(items) >= 2048 and np.all(items[:, 7] == 0)
+    cost = (items[:, 5] - items[:, 4]).astype(np.int64)
+    assert np.all(np.diff(cost) <= 0)
+    key = items[:, 0].astype(np.int64) * 1 << 40 | items[:, 1].astype(np.int64) << 32 | items[:, 4]
+    same = np.diff(cost) == 0
+    assert np.all(np.diff(key)[same] > 0)
+
+
 # ---------------------------------------------------------------- cascade decision
 def _brute_common_prefix(cu, sk, bt, BS, NB):
     B = len(sk)
