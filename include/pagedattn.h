@@ -45,9 +45,10 @@ typedef enum {
 /* Static string naming a status code. */
 const char* pa_status_str(pa_status s);
 
-/* Library version, (major << 16) | minor.  Major 2: pa_attn_params and
- * pa_plan_info carry sliding_window, reduce items carry the sequence's first
- * token (work-list version 2). */
+/* Library version, (major << 16) | minor.  Major 3: tiled work items of up
+ * to PA_TILED_ROWS_WIDE rows (pa_plan_info.tiled_rows; work-list version 3).  Major 2 added the sliding window
+ * to pa_attn_params and the plan info, and the sequence's first token to
+ * the reduce items. */
 int32_t pa_version(void);
 
 /* Head sizes with a compiled kernel. */
@@ -117,6 +118,9 @@ typedef struct {
   int32_t max_reduce_rows;   /* most rows of any reduce item                 */
   int32_t batch, num_heads, num_kv_heads, head_size, causal, num_tokens;
   int32_t sliding_window;    /* as planned (item key ranges start at the window) */
+  int32_t tiled_rows;        /* rows per tiled row block: PA_TILED_ROWS, or
+                                PA_TILED_ROWS_WIDE (8-wave workgroups sharing
+                                each K/V tile) */
   size_t worklist_bytes;
   size_t workspace_bytes;
 } pa_plan_info;
@@ -359,23 +363,27 @@ pa_status pa_merge_attn_states(void* out, float* out_lse,
  * items, PA_ITEM_WORDS words each.
  * attention item: seq, kv_head, row0, nrows, kv_begin, kv_end,
  *   partial_row (-1: write out/lse directly), kind (0: small-row item of
- *   <= PA_SMALL_MAX_ROWS rows, 1: tiled item of <= PA_TILED_ROWS rows),
+ *   <= PA_SMALL_MAX_ROWS rows, 1: tiled item of <= pa_plan_info.tiled_rows
+ *   rows: PA_TILED_ROWS_WIDE in launches with no small-row items at
+ *   head_size <= 128 whose prefills are long, else PA_TILED_ROWS),
  *   first token of the sequence (cu_seqlens_q[seq]), Lk - Lq of the
  *   sequence, 0, 0.  Rows and key range are clipped to the sequence, so the
  *   kernels read no lengths from device memory.
- *   When both kinds are present they are interleaved, longest estimated
- *   time first, and run as one launch; otherwise all items are one kind.
+ *   When both kinds are present they run as one launch: each kind longest
+ *   first, the two merged in proportion to their counts; otherwise all
+ *   items are one kind, longest first.
  * reduce item: seq, kv_head, row0, nrows, partial_row0, num_splits,
  *   first token of the sequence (cu_seqlens_q[seq]), 0, 0, 0, 0, 0
  *   (split s of the unit wrote rows partial_row0 + s * nrows ...)
  * A "row" of sequence b is (query token i, head-in-group g) -> row i*G + g,
  * G = H / Hkv; kv_head's query heads are kv_head*G .. kv_head*G + G-1.    */
 #define PA_WORKLIST_MAGIC 0x50414731
-#define PA_WORKLIST_VERSION 2
+#define PA_WORKLIST_VERSION 3
 #define PA_WORKLIST_HEADER_WORDS 16
 #define PA_ITEM_WORDS 12
 #define PA_SMALL_MAX_ROWS 16
 #define PA_TILED_ROWS 128
+#define PA_TILED_ROWS_WIDE 256
 
 #ifdef __cplusplus
 }

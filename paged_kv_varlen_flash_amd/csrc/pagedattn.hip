@@ -638,8 +638,11 @@ constexpr int tiled_lds_bytes() {
   return 2 * 64 * (D + 8) * 2 + 2 * 64 * (D + 32) * 2;
 }
 
-template <int D, bool FP8>
+// NW = 4: 128-row items; NW = 8: up to 256-row items, waves 0-3 load each
+// tile and all 8 waves compute on it
+template <int D, bool FP8, int NW = 4>
 __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* item, uint8_t* smem) {
+  static_assert(NW == 4 || NW == 8, "tiled workgroup");
   constexpr int NKT = D / 16;       // QK k-steps (16 d each)
   constexpr int NDT = D / 32;       // 32-wide d tiles of O^T
   constexpr int KP = D + 8;
@@ -658,6 +661,7 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
+  const bool loader = NW == 4 || tid < 256;   // the threads that move tiles
   const Item it = load_item(item);
   // the item carries the sequence's first token and causal offset, and its
   // rows and key range are already clipped to the sequence
@@ -681,6 +685,10 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
   const int wave_limit = a.causal ? (it.row0 + wave * 32) / G + it.koff : INT_MAX;
   const int wave_lo = a.window > 0 ? (it.row0 + wave * 32 + 31) / G + it.koff - (a.window - 1) : INT_MIN;
   const int row_lo = a.window > 0 ? tok + it.koff - (a.window - 1) : INT_MIN;
+  // 8-wave items: a wave skips the tiles that none of its rows sees (a
+  // wholly masked tile adds nothing), and a wave with no rows skips all
+  const bool wave_rows = wave * 32 < nrows;
+  const int wave_last = a.causal ? (it.row0 + min(wave * 32 + 31, nrows - 1)) / G + it.koff : INT_MAX;
 
   bf16x8_t qf[NKT];
   if (row_ok) {
@@ -979,8 +987,8 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
   constexpr bool VLOOKUP = !FP8 && D == 64;
   int ent = 0;
   if constexpr (!VLOOKUP) {
-    if (j0 < kv1) load_any(j0);
-  } else {
+    if (loader && j0 < kv1) load_any(j0);
+  } else if (loader) {
     if (j0 < kv1) load_tile_e(j0, fetch_entries(j0));
     if (j0 + 64 < kv1) ent = fetch_entries(j0 + 64);
   }
@@ -989,21 +997,23 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
   // treats the Q loads as possibly in flight inside the loop and makes
   // every QK MFMA wait for the next tile's prefetch loads as well
   __builtin_amdgcn_s_waitcnt(0);
-  if (j0 < kv1) store_any(0);
+  if (loader && j0 < kv1) store_any(0);
   __syncthreads();
   for (; j0 < kv1; j0 += 64, buf ^= 1) {
     const bool more = j0 + 64 < kv1;
     if constexpr (!VLOOKUP) {
-      if (more) load_any(j0 + 64);
-    } else if (more) {
+      if (more && loader) load_any(j0 + 64);
+    } else if (more && loader) {
       load_tile_e(j0 + 64, ent);
       if (j0 + 128 < kv1) ent = fetch_entries(j0 + 128);
     }
-    if (j0 + 64 > kv1 || j0 + 63 > wave_limit || j0 < wave_lo)
-      tile(j0, buf, Bool<true>{});
-    else
-      tile(j0, buf, Bool<false>{});
-    if (more) store_any(buf ^ 1);
+    if (NW == 4 || (wave_rows && j0 <= wave_last)) {
+      if (j0 + 64 > kv1 || j0 + 63 > wave_limit || j0 < wave_lo)
+        tile(j0, buf, Bool<true>{});
+      else
+        tile(j0, buf, Bool<false>{});
+    }
+    if (more && loader) store_any(buf ^ 1);
     __syncthreads();
   }
 
@@ -1046,6 +1056,18 @@ template <int D, bool FP8>
 __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_tiled_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[tiled_lds_bytes<D>()];
   tiled_body<D, FP8>(a, a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS, smem);
+}
+
+// Tiled attention for items of up to 256 rows (launches with no small-row
+// items, D <= 128): 8 waves of 32 rows share each K/V tile, so a tile is
+// loaded and stored to LDS once per 256 rows instead of once per 128; one
+// workgroup per compute unit holds the same 2 waves per SIMD as two
+// 4-wave workgroups.
+template <int D, bool FP8>
+__global__ __launch_bounds__(512, 2) void attn_tiled_wide_kernel(AttnArgs a) {
+  static_assert(D <= 128, "8 waves of a 256-row item fit the registers at D <= 128");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[tiled_lds_bytes<D>()];
+  tiled_body<D, FP8, 8>(a, a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1209,7 +1231,17 @@ pa_status launch_fwd(const AttnArgs& base, const pa_plan_info* plan, const int32
   } else if (plan->num_small_items > 0) {
     hipLaunchKernelGGL((attn_small_kernel<D, FP8>), dim3(plan->num_small_items), dim3(256), 0, stream, a);
   } else if (plan->num_tiled_items > 0) {
-    hipLaunchKernelGGL((attn_tiled_kernel<D, FP8>), dim3(plan->num_tiled_items), dim3(256), 0, stream, a);
+    bool launched = false;
+    if constexpr (D <= 128) {
+      if (plan->tiled_rows == PA_TILED_ROWS_WIDE) {
+        hipLaunchKernelGGL((attn_tiled_wide_kernel<D, FP8>), dim3(plan->num_tiled_items),
+                           dim3(512), 0, stream, a);
+        launched = true;
+      }
+    }
+    if (!launched)
+      hipLaunchKernelGGL((attn_tiled_kernel<D, FP8>), dim3(plan->num_tiled_items), dim3(256), 0,
+                         stream, a);
   }
   if (plan->num_reduce_items > 0) {
     const int32_t* r =
@@ -1307,7 +1339,12 @@ pa_status varlen_fwd(const pa_attn_params* p, const pa_plan_info* plan, const in
     return PA_ERR_INVALID_ARGUMENT;
   if (plan->num_small_items < 0 || plan->num_tiled_items < 0 || plan->num_reduce_items < 0 ||
       plan->num_partial_rows < 0 || plan->max_reduce_rows < 0 ||
-      plan->max_reduce_rows > PA_TILED_ROWS || (plan->num_reduce_items > 0 && plan->max_reduce_rows == 0))
+      plan->max_reduce_rows > plan->tiled_rows ||
+      (plan->num_reduce_items > 0 && plan->max_reduce_rows == 0))
+    return PA_ERR_INVALID_ARGUMENT;
+  // wide tiled blocks only in launches of tiled items alone, at D <= 128
+  if (plan->tiled_rows != PA_TILED_ROWS &&
+      (plan->tiled_rows != PA_TILED_ROWS_WIDE || plan->num_small_items > 0 || p->head_size > 128))
     return PA_ERR_INVALID_ARGUMENT;
   const int64_t n_items =
       (int64_t)plan->num_small_items + plan->num_tiled_items + plan->num_reduce_items;

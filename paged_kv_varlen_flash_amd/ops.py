@@ -30,6 +30,8 @@ PA_ERR_HIP = 4
 PA_WORKLIST_MAGIC = 0x50414731
 PA_WORKLIST_HEADER_WORDS = 16
 PA_ITEM_WORDS = 12
+PA_TILED_ROWS = 128             # tiled item rows in launches with small-row items, or at D = 256
+PA_TILED_ROWS_WIDE = 256        # tiled item rows otherwise
 PLAN_TARGET_CUS = 256          # compute units the planner schedules for (PA_PLAN_TARGET_CUS)
 
 EXPORTED = ["pa_status_str", "pa_version", "pa_supported_head_sizes", "pa_plan_varlen",
@@ -63,7 +65,7 @@ class PlanInfo(ctypes.Structure):
                 ("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_size", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
-                ("sliding_window", ctypes.c_int32),
+                ("sliding_window", ctypes.c_int32), ("tiled_rows", ctypes.c_int32),
                 ("worklist_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t)]
 
     def as_dict(self):

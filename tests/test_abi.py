@@ -43,7 +43,7 @@ def test_status_strings_and_version(L):
     assert ops.status_str(0) == "PA_OK"
     assert ops.status_str(3) == "PA_ERR_WORKSPACE_TOO_SMALL"
     assert ops.status_str(99) == "PA_ERR_UNKNOWN"
-    assert L.pa_version() >> 16 == 2
+    assert L.pa_version() >> 16 == 3
     assert ops.supported_head_sizes() == [64, 128, 256]
 
 
@@ -219,7 +219,7 @@ def test_cascade_split(L):
 
 # ---------------------------------------------------------------- plan coverage
 def parse(wl_words, info):
-    assert wl_words[0] == ops.PA_WORKLIST_MAGIC and wl_words[1] == 2
+    assert wl_words[0] == ops.PA_WORKLIST_MAGIC and wl_words[1] == 3
     n_att = info.num_small_items + info.num_tiled_items
     IW = ops.PA_ITEM_WORDS
     items = wl_words[16:16 + IW * n_att].reshape(-1, IW)
@@ -245,9 +245,14 @@ def check_plan_covers(H, Hkv, q_lens, k_lens, causal, force_splits=0):
     # words 8, 9: the sequence's first token and Lk - Lq
     assert np.array_equal(items[:, 8], cu[items[:, 0]])
     assert np.array_equal(items[:, 9], np.asarray(k_lens)[items[:, 0]] - np.diff(cu)[items[:, 0]])
+    # tiled items hold up to 256 rows in plans without small-row items at D <= 128
+    assert info.tiled_rows in (ops.PA_TILED_ROWS, ops.PA_TILED_ROWS_WIDE)
+    if info.num_small_items > 0:
+        assert info.tiled_rows == ops.PA_TILED_ROWS
+    tiled_max = info.tiled_rows
     for idx, (seq, kvh, row0, nrows, k0, k1, prow, kind, *_) in enumerate(items):
         is_small = kind == 0
-        assert nrows <= (PA_SMALL if is_small else 128) and nrows >= 1
+        assert nrows <= (PA_SMALL if is_small else tiled_max) and nrows >= 1
         for r in range(row0, row0 + nrows):
             cover.setdefault((seq, kvh, r), []).append((k0, k1, prow))
     seen_prow = set()

@@ -79,6 +79,7 @@ FP8_SHAPES = [
     (64, 8, 1, 48, True, ((40, 40), (17, 300), (250, 260)), 0),
     (128, 4, 2, 16, False, ((64, 64), (33, 97), (200, 450)), 2),
     (256, 4, 1, 32, True, ((70, 70), (33, 180)), 0),
+    (128, 4, 2, 32, True, ((2100, 2100), (2050, 2200)), 0),   # 256-row tiled blocks
 ]
 
 

@@ -199,6 +199,9 @@ PREFILL_ONLY = [
     (64, 2, 3, 64, False, ((100, 130), (9, 9)), 2),
     (128, 1, 2, 16, True, ((600, 600), (20, 10)), 5),
     (256, 4, 1, 32, True, ((70, 70), (33, 180)), 0),
+    # long enough for 256-row blocks at D = 128 (2048+ query tokens on average)
+    (128, 4, 2, 32, True, ((2100, 2100), (2050, 2400)), 0),
+    (128, 4, 2, 16, False, ((2300, 2300), (1900, 2000)), 3),
 ]
 
 
@@ -211,6 +214,9 @@ def test_prefill_only(case):
         f"force={force}")
     plan = _check_case(spec, np.random.default_rng(7000 + case), force, f"prefill_only{case}")
     assert plan.info.num_small_items == 0 and plan.info.num_tiled_items > 0
+    # 256-row blocks (8-wave workgroups) at D = 64, or for long prefills at D = 128
+    wide = D <= 64 or (D <= 128 and np.mean([q for q, _ in seqs]) >= 2048)
+    assert plan.info.tiled_rows == (256 if wide else 128)
 
 
 def _check_case(spec, rng, force, label, qmul=1.0, smul=1.0):
