@@ -9,6 +9,9 @@
 //                              head), bound by HBM reads of K/V
 //   attn_tiled_kernel<D>       paged attention for 128-row blocks (prefill),
 //                              bound by the matrix cores
+//   attn_tiled_wide_kernel<D>  the same for 256-row blocks: 8 waves share
+//                              each K/V tile (long prefills, D <= 128)
+//   attn_mixed_kernel<D>       small-row and 128-row items in one launch
 //   split_reduce_kernel<D>     LSE merge of split-KV partials (section 1.3
 //                              num_splits)
 //   merge_states_kernel        two-way LSE merge (section 6.3, step 3)
