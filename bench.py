@@ -355,8 +355,8 @@ def main():
         line["cpu_baseline"] = head["cpu"]
     if args.secondary:
         sec = {}
-        for name in ("chunked_prefill_mix", "chunked_prefill_mix_prefill", "long_decode_d256",
-                     "cascade_prefix"):
+        for name in ("chunked_prefill_mix", "chunked_prefill_mix_prefill", "prefill_causal_8k",
+                     "long_decode_d256", "cascade_prefix"):
             r = measure(name, args, dev, flush, False)
             w = r["wl"]
             ent = {"ms_per_step": round(r["ms_per_step"], 4),
@@ -373,7 +373,7 @@ def main():
                 one = measure(name, args, dev, flush, False, single_pass=True)
                 ent["single_pass_attn_avg_us"] = round(one["attn_mean_s"] * 1e6, 2)
                 ent["cascade_decision"] = {"common_prefix_len": P, "use_cascade": use}
-            if name.startswith("chunked_prefill_mix"):
+            if name.startswith("chunked_prefill_mix") or name.startswith("prefill_"):
                 ent["attn_TFLOPs"] = round(r["flops"] / r["attn_mean_s"] / 1e12, 1)
                 ent["mfma_frac"] = round(r["flops"] / r["attn_mean_s"] / 1e12 / BF16_PEAK_TFLOPS, 4)
             sec[name] = ent

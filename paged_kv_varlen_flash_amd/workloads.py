@@ -94,6 +94,11 @@ SPECS = {
         block_size=32, causal=True, seed=1003, groups=(("prefill", 8, 256, 2048),),
         description="the 8 causal prefills of chunked_prefill_mix alone (the same seed draws "
                     "the same lengths first); H=32 Hkv=8 D=128 BS=32"),
+    "prefill_causal_8k": Spec(
+        name="prefill_causal_8k", num_heads=32, num_kv_heads=8, head_size=128, block_size=32,
+        causal=True, seed=1010, groups=(("prefill", 4, 8192, 8192),),
+        description="4 causal prefills of 8192 tokens; H=32 Hkv=8 D=128 BS=32 (long-prefill "
+                    "counterpart of chunked_prefill_mix_prefill)"),
     "cascade_prefix": Spec(
         name="cascade_prefix", num_heads=32, num_kv_heads=8, head_size=128, block_size=16,
         causal=True, seed=1004, groups=(("decode", 32, 64, 512),), shared_prefix=2048,
