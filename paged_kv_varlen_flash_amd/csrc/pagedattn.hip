@@ -688,8 +688,10 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
   const int wave_limit = a.causal ? (it.row0 + wave * 32) / G + it.koff : INT_MAX;
   const int wave_lo = a.window > 0 ? (it.row0 + wave * 32 + 31) / G + it.koff - (a.window - 1) : INT_MIN;
   const int row_lo = a.window > 0 ? tok + it.koff - (a.window - 1) : INT_MIN;
-  // 8-wave items: a wave skips the tiles that none of its rows sees (a
-  // wholly masked tile adds nothing), and a wave with no rows skips all
+  // a wave skips the tiles that none of its rows sees (a wholly masked tile
+  // adds nothing: the causal end of a block's last tile, and every tile of
+  // the 8-wave items' second half-block past its rows), and a wave with no
+  // rows skips all
   const bool wave_rows = wave * 32 < nrows;
   const int wave_last = a.causal ? (it.row0 + min(wave * 32 + 31, nrows - 1)) / G + it.koff : INT_MAX;
 
@@ -1010,7 +1012,7 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
       load_tile_e(j0 + 64, ent);
       if (j0 + 128 < kv1) ent = fetch_entries(j0 + 128);
     }
-    if (NW == 4 || (wave_rows && j0 <= wave_last)) {
+    if (wave_rows && j0 <= wave_last) {
       if (j0 + 64 > kv1 || j0 + 63 > wave_limit || j0 < wave_lo)
         tile(j0, buf, Bool<true>{});
       else
