@@ -612,11 +612,13 @@ __global__ __launch_bounds__(256, (D <= 128 ? (FP8 ? 4 : 3) : 1)) void attn_smal
 }
 
 // ---------------------------------------------------------------------------
-// Tiled attention: one workgroup of 4 waves per 128-row block; wave w owns
-// rows 32w..32w+31 (lane (n = lane%32, h = lane/32) owns row n and the key
-// half h of each 32x32 MFMA tile).  Key tiles of 64 keys are gathered
-// through the block table by all 256 threads into registers one tile ahead
-// (16 consecutive lanes per 256-byte key row), then stored to LDS: K with a
+// Tiled attention: one workgroup of 4 waves per 128-row block (8 waves per
+// 256-row block in the wide kernel); wave w owns rows 32w..32w+31 (lane
+// (n = lane%32, h = lane/32) owns row n and the key half h of each 32x32
+// MFMA tile).  Key tiles of 64 keys are gathered through the block table by
+// threads 0..255 into registers one tile ahead (16 consecutive lanes per
+// 256-byte key row, one bounds-checked buffer load per plane per 16 keys),
+// then stored to LDS, where every wave of the workgroup reads them: K with a
 // pitch of D+8 elements (conflict-free 16-byte operand reads), V with D+32
 // (the transposing reads of two 16-lane groups cover all banks once).
 //
