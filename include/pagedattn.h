@@ -46,9 +46,9 @@ typedef enum {
 const char* pa_status_str(pa_status s);
 
 /* Library version, (major << 16) | minor.  Major 3: tiled work items of up
- * to PA_TILED_ROWS_WIDE rows (pa_plan_info.tiled_rows; work-list version 3).  Major 2 added the sliding window
- * to pa_attn_params and the plan info, and the sequence's first token to
- * the reduce items. */
+ * to PA_TILED_ROWS_WIDE rows, reported in pa_plan_info.tiled_rows (work-list
+ * version 3).  Major 2 added the sliding window to pa_attn_params and the
+ * plan info, and the sequence's first token to the reduce items. */
 int32_t pa_version(void);
 
 /* Head sizes with a compiled kernel. */
