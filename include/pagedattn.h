@@ -112,7 +112,7 @@ typedef struct {
 
 typedef struct {
   int32_t num_small_items;   /* items for the small-row (decode) kernel     */
-  int32_t num_tiled_items;   /* items for the 128-row tiled kernel           */
+  int32_t num_tiled_items;   /* items for the tiled kernels (<= tiled_rows)  */
   int32_t num_reduce_items;  /* split-KV merges                              */
   int32_t num_partial_rows;  /* fp32 partial rows held in the workspace      */
   int32_t max_reduce_rows;   /* most rows of any reduce item                 */
