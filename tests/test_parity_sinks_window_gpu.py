@@ -24,6 +24,11 @@ CASES = [
     (256, 8, 2, 64, ((1, 3000), (1, 700)), 1000, True, 0, False),
     (128, 4, 2, 32, ((1, 700), (90, 400), (1, 64), (130, 130)), 0, True, 0, False),
     (128, 4, 2, 32, ((1, 700), (90, 400), (1, 64)), 0, True, 3, True),
+    # prefill-only batches on 256-row blocks (8-wave workgroups): D = 64, and
+    # prefills of 2000+ tokens at D = 128, with windows, sinks, splits, E4M3
+    (64, 4, 2, 32, ((300, 300), (100, 400)), 64, True, 0, False),
+    (128, 4, 2, 32, ((2100, 2100), (2050, 2300)), 700, True, 0, False),
+    (128, 4, 2, 16, ((2200, 2200), (2000, 2000)), 1500, True, 2, True),
 ]
 
 
