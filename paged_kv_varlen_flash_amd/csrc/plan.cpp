@@ -244,7 +244,9 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
     const int64_t chunk = std::max<int64_t>(
         kSmallMinChunk,
         ceil_div(ceil_div(std::max<int64_t>(small_keys, 1),
-                          (int64_t)(target * kSmallItemsPerCu)), 64) * 64);
+                          (int64_t)(target * (p->head_size >= 256 ? kSmallItemsPerCuD256
+                                                                  : kSmallItemsPerCu))),
+                 64) * 64);
     for (const Unit& u : units) {
       if (!u.small) continue;
       const size_t first = small_items.size();

@@ -21,6 +21,10 @@ constexpr int kSmallWaves = 4;
 constexpr int kSmallStep = 16;
 constexpr int kSmallMinChunk = 256;
 constexpr double kSmallItemsPerCu = 3.5;
+// at D = 256 one small-row workgroup fits a compute unit (three or four at
+// D <= 128): 2.5 measured best of 2 ... 4 on the long-context decode batch
+// (16 sequences of 32K-128K keys: 454 us against 464 us at 3.5)
+constexpr double kSmallItemsPerCuD256 = 2.5;
 
 static_assert(PA_TILED_ROWS == kTiledWaves * 32, "tiled row block");
 
