@@ -74,7 +74,7 @@ class Step:
             d["v_scale"] = torch.from_numpy(self.v_scale).to(dev)
         self.params = ops.make_params(wl.B, wl.H, wl.Hkv, wl.D, wl.BS, wl.num_blocks,
                                       wl.block_table.shape[1], wl.causal, wl.scale,
-                                      sliding_window=window)
+                                      sliding_window=window, kv_cache_fp8=fp8)
         self.s_aux = None
         if sinks:
             rng = np.random.default_rng(4002)

@@ -83,6 +83,12 @@ typedef struct {
   float scale;
   int32_t sliding_window;   /* 0: none; W > 0 (causal only): query i sees keys
                                i + Lk - Lq - (W - 1) .. i + Lk - Lq */
+  int32_t kv_cache_fp8;     /* 0: bf16 cache, 1: E4M3 cache (pa_varlen_fwd_fp8).
+                               Read by the planner only: in a launch with no
+                               tiled items it cuts key ranges finer for the
+                               smaller cache.  A plan is valid with either
+                               cache; only its split count differs.  Other
+                               values: PA_ERR_INVALID_ARGUMENT */
 } pa_attn_params;
 
 /* ------------------------------------------------------------------------

@@ -40,6 +40,7 @@ pa_status check_params(const pa_attn_params* p) {
     return PA_ERR_INVALID_ARGUMENT;
   if ((int64_t)p->max_blocks_per_seq * p->block_size > INT32_MAX / 2) return PA_ERR_INVALID_ARGUMENT;
   if (p->causal != 0 && p->causal != 1) return PA_ERR_INVALID_ARGUMENT;
+  if (p->kv_cache_fp8 != 0 && p->kv_cache_fp8 != 1) return PA_ERR_INVALID_ARGUMENT;
   // a sliding window is the causal band of its last W keys
   if (p->sliding_window < 0 || (p->sliding_window > 0 && !p->causal)) return PA_ERR_INVALID_ARGUMENT;
   // a softmax scale is positive (the kernels take row maxima on unscaled scores)
@@ -245,7 +246,9 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
         kSmallMinChunk,
         ceil_div(ceil_div(std::max<int64_t>(small_keys, 1),
                           (int64_t)(target * (p->head_size >= 256 ? kSmallItemsPerCuD256
-                                                                  : kSmallItemsPerCu))),
+                                              : p->kv_cache_fp8 && n_tiled == 0
+                                                  ? kSmallItemsPerCuFp8
+                                                  : kSmallItemsPerCu))),
                  64) * 64);
     for (const Unit& u : units) {
       if (!u.small) continue;
@@ -389,7 +392,7 @@ const char* pa_status_str(pa_status s) {
   return "PA_ERR_UNKNOWN";
 }
 
-int32_t pa_version(void) { return (3 << 16) | 0; }
+int32_t pa_version(void) { return (3 << 16) | 1; }
 
 pa_status pa_plan_varlen(const pa_attn_params* p, const int32_t* host_cu_seqlens_q,
                          const int32_t* host_seqused_k, int32_t force_splits,

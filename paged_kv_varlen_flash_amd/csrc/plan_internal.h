@@ -16,7 +16,7 @@ constexpr int kTiledMinChunk = 256;
 // small-row kernel: 4 waves taking 16-key steps in turn; the planner cuts
 // key ranges into pieces of at least kSmallMinChunk keys so that there are
 // about kSmallItemsPerCu workgroups per compute unit (of 2.5 ... 5, measured
-// on MI355X, 3.5 suits the bf16 and the E4M3 decode batches together best)
+// on MI355X, 3.5 suits the bf16 decode batch and chunked-prefill mixes best)
 constexpr int kSmallWaves = 4;
 constexpr int kSmallStep = 16;
 constexpr int kSmallMinChunk = 256;
@@ -25,6 +25,12 @@ constexpr double kSmallItemsPerCu = 3.5;
 // D <= 128): 2.5 measured best of 2 ... 4 on the long-context decode batch
 // (16 sequences of 32K-128K keys: 454 us against 464 us at 3.5)
 constexpr double kSmallItemsPerCuD256 = 2.5;
+// an E4M3 cache halves each piece's bytes and fits four small-row workgroups
+// per compute unit at D <= 128: 4.5 measured best of 3.5 ... 5 on the 64-
+// sequence decode batch (60.4 us against 62.3 us at 3.5 and 62.0 us at 5).
+// Used for launches of small items only: with tiled items beside them (a
+// chunked-prefill mix) 3.5 stays faster, 183-185 us against 187-189 us.
+constexpr double kSmallItemsPerCuFp8 = 4.5;
 
 static_assert(PA_TILED_ROWS == kTiledWaves * 32, "tiled row block");
 

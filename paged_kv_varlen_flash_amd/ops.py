@@ -52,7 +52,7 @@ class AttnParams(ctypes.Structure):
                 ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
                 ("max_blocks_per_seq", ctypes.c_int32), ("block_table_stride", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("sliding_window", ctypes.c_int32)]
+                ("sliding_window", ctypes.c_int32), ("kv_cache_fp8", ctypes.c_int32)]
 
     def __repr__(self):
         return "AttnParams(" + ", ".join(f"{k}={getattr(self, k)}" for k, _ in self._fields_) + ")"
@@ -155,11 +155,11 @@ def _ptr_i32(a: Optional[np.ndarray]):
 
 def make_params(batch, num_heads, num_kv_heads, head_size, block_size, num_blocks,
                 max_blocks_per_seq, causal, scale, block_table_stride=0,
-                sliding_window=0) -> AttnParams:
+                sliding_window=0, kv_cache_fp8=False) -> AttnParams:
     return AttnParams(int(batch), int(num_heads), int(num_kv_heads), int(head_size),
                       int(block_size), int(num_blocks), int(max_blocks_per_seq),
                       int(block_table_stride), int(bool(causal)), float(np.float32(scale)),
-                      int(sliding_window))
+                      int(sliding_window), int(bool(kv_cache_fp8)))
 
 
 # --------------------------------------------------------------------------
@@ -361,13 +361,14 @@ class VarlenPlan:
 
 def plan_varlen(q_shape, kv_cache_shape, block_table_shape, host_cu_seqlens_q, host_seqused_k,
                 scale, causal, force_splits=0, block_table_stride=0,
-                sliding_window=0) -> VarlenPlan:
+                sliding_window=0, kv_cache_fp8=False) -> VarlenPlan:
     T, H, D = q_shape
     _, NB, BS, Hkv, D2 = kv_cache_shape
     if D2 != D:
         raise ValueError("head size of q and kv_cache differ")
     B, MB = block_table_shape
-    p = make_params(B, H, Hkv, D, BS, NB, MB, causal, scale, block_table_stride, sliding_window)
+    p = make_params(B, H, Hkv, D, BS, NB, MB, causal, scale, block_table_stride, sliding_window,
+                    kv_cache_fp8)
     return VarlenPlan(p, host_cu_seqlens_q, host_seqused_k, force_splits)
 
 

@@ -44,6 +44,7 @@ def test_status_strings_and_version(L):
     assert ops.status_str(3) == "PA_ERR_WORKSPACE_TOO_SMALL"
     assert ops.status_str(99) == "PA_ERR_UNKNOWN"
     assert L.pa_version() >> 16 == 3
+    assert L.pa_version() & 0xFFFF >= 1          # pa_attn_params.kv_cache_fp8
     assert ops.supported_head_sizes() == [64, 128, 256]
 
 
@@ -228,14 +229,15 @@ def parse(wl_words, info):
     return items, red
 
 
-def check_plan_covers(H, Hkv, q_lens, k_lens, causal, force_splits=0):
+def check_plan_covers(H, Hkv, q_lens, k_lens, causal, force_splits=0, kv_cache_fp8=False):
     """Every visible (row, key) pair is covered by exactly one item; split
     units have a reduce item whose partial rows match their items."""
     G = H // Hkv
     cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
     BS = 16
     MB = max(1, max((k + BS - 1) // BS for k in k_lens))
-    p = ops.make_params(len(q_lens), H, Hkv, 64, BS, 4096, MB, causal, 0.1)
+    p = ops.make_params(len(q_lens), H, Hkv, 64, BS, 4096, MB, causal, 0.1,
+                        kv_cache_fp8=kv_cache_fp8)
     words, info = ops.pa_plan_varlen(p, cu, k_lens, force_splits)
     items, red = parse(words, info)
     cover = {}
@@ -341,6 +343,26 @@ def test_small_items_longest_first(L):
         if prow >= 0 and k1 != wl.k_lens[seq]:
             assert (k1 - k0) % 64 == 0 and k0 % 64 == 0
 
+
+
+def test_fp8_cache_plan(L):
+    """An E4M3 cache only changes how finely decode key ranges are cut: the
+    plan still covers every (row, key) pair once, with no fewer items."""
+    rng = np.random.default_rng(31)
+    k_lens = rng.integers(512, 4097, 64).astype(np.int32)
+    q_lens = np.ones(64, np.int32)
+    check_plan_covers(32, 8, q_lens, k_lens, False, kv_cache_fp8=True)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    n = []
+    for fp8 in (False, True):
+        p = ops.make_params(64, 32, 8, 128, 16, 20000, 256, False, 0.1, kv_cache_fp8=fp8)
+        n.append(ops.pa_plan_varlen(p, cu, k_lens)[1].num_small_items)
+    assert n[1] > n[0]
+    p = params()
+    p.kv_cache_fp8 = 2
+    with pytest.raises(ops.PaError) as e:
+        ops.pa_plan_varlen(p, CU, SK)
+    assert e.value.status == ops.PA_ERR_INVALID_ARGUMENT
 
 def test_mixed_launch_order(L):
     """A mixed launch lists each kind longest first, merged in proportion to

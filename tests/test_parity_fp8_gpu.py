@@ -35,7 +35,8 @@ def _run_fp8(wl, seed, force_splits=0):
     kst, vst = _f32(ks), _f32(vs)
     ops.pa_reshape_and_cache_fp8(d["key"], d["value"], cache, d["slot_mapping"], kst, vst)
     plan = ops.plan_varlen(tuple(d["q"].shape), tuple(cache.shape), tuple(d["block_table"].shape),
-                           wl.cu_seqlens_q, wl.k_lens, wl.scale, wl.causal, force_splits=force_splits)
+                           wl.cu_seqlens_q, wl.k_lens, wl.scale, wl.causal, force_splits=force_splits,
+                           kv_cache_fp8=True)
     out = torch.full_like(d["q"], float("nan"))
     lse = torch.full((wl.T, wl.H), float("nan"), dtype=torch.float32, device="cuda")
     ops.varlen_fwd(d["q"], cache, d["cu_seqlens_q"], d["seqused_k"], d["block_table"], plan,

@@ -71,7 +71,7 @@ def test_sinks_and_window(case):
         ks = vs = kst = vst = None
         tc = torch.from_numpy(cache.view(np.int16)).cuda().view(torch.bfloat16)
     scale = np.float32(1.0 / np.sqrt(D))
-    p = ops.make_params(B, H, Hkv, D, BS, NB, MB, True, scale, sliding_window=win)
+    p = ops.make_params(B, H, Hkv, D, BS, NB, MB, True, scale, sliding_window=win, kv_cache_fp8=fp8)
     plan = ops.VarlenPlan(p, cu, k_lens, force)
     if force:
         assert plan.info.num_reduce_items > 0
