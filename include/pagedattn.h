@@ -45,9 +45,10 @@ typedef enum {
 /* Static string naming a status code. */
 const char* pa_status_str(pa_status s);
 
-/* Library version, (major << 16) | minor.  Major 3: tiled work items of up
- * to PA_TILED_ROWS_WIDE rows, reported in pa_plan_info.tiled_rows (work-list
- * version 3).  Major 2 added the sliding window to pa_attn_params and the
+/* Library version, (major << 16) | minor.  Major 4 added kv_cache_fp8 to
+ * pa_attn_params (the work list is unchanged, version 3).  Major 3: tiled
+ * work items of up to PA_TILED_ROWS_WIDE rows, reported in
+ * pa_plan_info.tiled_rows (work-list version 3).  Major 2 added the sliding window to pa_attn_params and the
  * plan info, and the sequence's first token to the reduce items. */
 int32_t pa_version(void);
 

@@ -392,7 +392,7 @@ const char* pa_status_str(pa_status s) {
   return "PA_ERR_UNKNOWN";
 }
 
-int32_t pa_version(void) { return (3 << 16) | 1; }
+int32_t pa_version(void) { return (4 << 16) | 0; }
 
 pa_status pa_plan_varlen(const pa_attn_params* p, const int32_t* host_cu_seqlens_q,
                          const int32_t* host_seqused_k, int32_t force_splits,

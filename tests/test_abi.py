@@ -43,8 +43,7 @@ def test_status_strings_and_version(L):
     assert ops.status_str(0) == "PA_OK"
     assert ops.status_str(3) == "PA_ERR_WORKSPACE_TOO_SMALL"
     assert ops.status_str(99) == "PA_ERR_UNKNOWN"
-    assert L.pa_version() >> 16 == 3
-    assert L.pa_version() & 0xFFFF >= 1          # pa_attn_params.kv_cache_fp8
+    assert L.pa_version() >> 16 == 4              # pa_attn_params.kv_cache_fp8
     assert ops.supported_head_sizes() == [64, 128, 256]
 
 
