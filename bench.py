@@ -45,8 +45,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_llama8b")
     ap.add_argument("--kernel-reps", type=int, default=30)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="budget for the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="budget for each oracle CPU baseline")
+    ap.add_argument("--prefill-workload", default="chunked_prefill_mix_prefill",
+                    help="causal-prefill workload of the line's prefill object")
+    ap.add_argument("--mixed-workload", default="chunked_prefill_mix",
+                    help="decode+prefill workload of the line's mixed object")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time the --workload only (no prefill or mixed object)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary", action="store_true",
                     help="also time the prefill mix and the long-context decode")
@@ -74,7 +80,8 @@ class Step:
             d["v_scale"] = torch.from_numpy(self.v_scale).to(dev)
         self.params = ops.make_params(wl.B, wl.H, wl.Hkv, wl.D, wl.BS, wl.num_blocks,
                                       wl.block_table.shape[1], wl.causal, wl.scale,
-                                      sliding_window=window, kv_cache_fp8=fp8)
+                                      sliding_window=window, kv_cache_fp8=fp8,
+                                      num_cus=ops.device_cus(dev))
         self.s_aux = None
         if sinks:
             rng = np.random.default_rng(4002)
@@ -230,21 +237,31 @@ def blas_threads():
         return 1
 
 
-def cpu_baseline(wl, budget_s, fp8_step=None):
-    """The fp64 oracle (as it stands) on whole sequences of the same batch
-    until the time budget is used; KV-read GB/s over the sequences done."""
+def _cores():
+    """Threads the oracle uses (its products run in BLAS) and the host cores
+    this process may run on."""
+    return {"cores": blas_threads(), "affinity_cores": len(os.sched_getaffinity(0))}
+
+
+def _oracle_cache(wl, fp8_step):
     import oracle.attention as OA
-    scales = {}
-    es = 2
     if fp8_step is None:
-        cache = OA.reshape_and_cache(wl.key, wl.value, wl.kv_cache, wl.slot_mapping)
-    else:
-        import oracle.fp8 as OF8
-        ks, vs = fp8_step.k_scale, fp8_step.v_scale
-        cache = OF8.reshape_and_cache_fp8(wl.key, wl.value, fp8_step.codes, wl.slot_mapping, ks, vs)
-        scales = {"k_scale": ks, "v_scale": vs}
-        es = 1
-    done, nbytes = 0, 0
+        return OA.reshape_and_cache(wl.key, wl.value, wl.kv_cache, wl.slot_mapping), {}, 2
+    import oracle.fp8 as OF8
+    ks, vs = fp8_step.k_scale, fp8_step.v_scale
+    cache = OF8.reshape_and_cache_fp8(wl.key, wl.value, fp8_step.codes, wl.slot_mapping, ks, vs)
+    return cache, {"k_scale": ks, "v_scale": vs}, 1
+
+
+def cpu_baseline(wl, budget_s, fp8_step=None, unit="GB/s"):
+    """The fp64 oracle (as it stands) on whole sequences of the same batch,
+    cycling through them until the time budget is used.  unit "GB/s": KV
+    bytes read per second; "TFLOP/s": the algorithmic flops (4·D·H per
+    visible (query, key) pair) of the sequences done per second."""
+    import oracle.attention as OA
+    cache, scales, es = _oracle_cache(wl, fp8_step)
+    pairs = wl.causal_pairs()
+    done, nbytes, flops = 0, 0, 0
     t0 = time.perf_counter()
     # whole sequences, cycling through the batch, until the budget is spent
     while time.perf_counter() - t0 < budget_s:
@@ -253,18 +270,20 @@ def cpu_baseline(wl, budget_s, fp8_step=None):
         OA.varlen_attention(wl.q[t_a:t_b], cache, np.array([0, t_b - t_a]), wl.k_lens[b:b + 1],
                             wl.block_table[b:b + 1], wl.scale, wl.causal, **scales)
         nbytes += 2 * int(wl.k_lens[b]) * wl.Hkv * wl.D * es
+        flops += 4 * wl.D * wl.H * int(pairs[b])
         done += 1
     el = time.perf_counter() - t0
-    return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": blas_threads(),
-            "kind": "oracle",
-            "sample": f"{done} sequence passes over the {wl.B} sequences of {wl.spec.name} "
-                      f"({nbytes/1e6:.1f} MB of KV), fp64 numpy, {el:.1f} s wall"}
+    val = nbytes / el / 1e9 if unit == "GB/s" else flops / el / 1e12
+    return dict({"value": round(val, 6 if unit != "GB/s" else 4), "unit": unit, "kind": "oracle",
+                 "sample": f"{done} whole-sequence passes over the {wl.B} sequences of "
+                           f"{wl.spec.name} ({nbytes/1e6:.1f} MB of KV, {flops/1e9:.2f} GFLOP), "
+                           f"fp64 numpy, {el:.1f} s wall"}, **_cores())
 
 
 _WORKLOADS = {}
 
 
-def measure(name, args, dev, flush, with_cpu, fp8=False, single_pass=False, window=0,
+def measure(name, args, dev, flush, cpu_unit=None, fp8=False, single_pass=False, window=0,
             sinks=False):
     import torch
     from paged_kv_varlen_flash_amd import workloads as W
@@ -273,6 +292,7 @@ def measure(name, args, dev, flush, with_cpu, fp8=False, single_pass=False, wind
         _WORKLOADS[name] = W.make(name)
     wl = _WORKLOADS[name]
     step = Step(wl, dev, fp8, single_pass, window, sinks)
+    print(f"bench: timing {name}{' (E4M3 cache)' if fp8 else ''}", file=sys.stderr, flush=True)
     per_step = time_steps(step, args.steps, args.warmup)
     t_mean, t_med = time_attention(step, args.kernel_reps, flush)
     kv = wl.kv_read_bytes() // (2 if fp8 else 1)
@@ -283,11 +303,104 @@ def measure(name, args, dev, flush, with_cpu, fp8=False, single_pass=False, wind
     flops = wl.attention_flops()
     res = {"workload": name, "wl": wl, "ms_per_step": per_step * 1e3, "attn_mean_s": t_mean,
            "attn_median_s": t_med, "kv_bytes": kv, "flops": flops, "plan": step.info.as_dict()}
-    if with_cpu:
-        res["cpu"] = cpu_baseline(wl, args.cpu_seconds, step if fp8 else None)
+    if cpu_unit:
+        print(f"bench: oracle CPU baseline on {name}", file=sys.stderr, flush=True)
+        res["cpu"] = cpu_baseline(wl, args.cpu_seconds, step if fp8 else None, cpu_unit)
     del step
     torch.cuda.empty_cache()
     return res
+
+
+def kernel_names(res, fp8):
+    """The kernels of one attention call, from its plan."""
+    p, D = res["plan"], res["wl"].D
+    tag = f"<{D}{', fp8' if fp8 else ''}>"
+    if p["num_small_items"] and p["num_tiled_items"]:
+        k = ["attn_mixed_kernel" + tag]
+    elif p["num_small_items"]:
+        k = ["attn_small_kernel" + tag]
+    elif p["tiled_rows"] == 256:
+        k = ["attn_tiled_wide_kernel" + tag]
+    else:
+        k = ["attn_tiled_kernel" + tag]
+    if p["num_reduce_items"]:
+        k.append(f"split_reduce_kernel<{D}>")
+    return " + ".join(k)
+
+
+def hbm_roofline(res, fp8, traffic_key):
+    ach = res["kv_bytes"] / res["attn_mean_s"] / 1e9
+    tr = recorded_traffic(traffic_key)
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4),
+            "traffic": (tr["read_bytes"] + tr["write_bytes"]) if tr else None,
+            "traffic_read_over_algorithmic": (round(tr["read_bytes"] / res["kv_bytes"], 4)
+                                              if tr else None),
+            "kernel": "pa_varlen_fwd%s: %s" % ("_fp8" if fp8 else "", kernel_names(res, fp8)),
+            "per_launch_bytes": res["kv_bytes"],
+            "avg_launch_us": round(res["attn_mean_s"] * 1e6, 2),
+            "median_launch_us": round(res["attn_median_s"] * 1e6, 2)}
+
+
+def mfma_roofline(res, fp8, traffic_key):
+    ach = res["flops"] / res["attn_mean_s"] / 1e12
+    tr = recorded_traffic(traffic_key)
+    return {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+            "traffic": (tr["read_bytes"] + tr["write_bytes"]) if tr else None,
+            "kernel": "pa_varlen_fwd%s: %s" % ("_fp8" if fp8 else "", kernel_names(res, fp8)),
+            "per_launch_flops": res["flops"],
+            "avg_launch_us": round(res["attn_mean_s"] * 1e6, 2),
+            "median_launch_us": round(res["attn_median_s"] * 1e6, 2)}
+
+
+def is_decode_like(wl, name):
+    return wl.q_lens.max() * (wl.H // wl.Hkv) <= 16 or name == "cascade_prefix"
+
+
+def entry(res, fp8, tkey):
+    """Step throughput, roofline and CPU baseline of one measured workload."""
+    wl = res["wl"]
+    if is_decode_like(wl, res["workload"]):
+        value, unit = res["kv_bytes"] / (res["ms_per_step"] * 1e-3) / 1e9, "GB/s"
+        roof = hbm_roofline(res, fp8, tkey)
+    else:
+        value, unit = res["flops"] / (res["ms_per_step"] * 1e-3) / 1e12, "TFLOP/s"
+        roof = mfma_roofline(res, fp8, tkey)
+    e = {"workload": res["workload"], "value": round(value, 1), "unit": unit,
+         "ms_per_step": round(res["ms_per_step"], 4), "config": wl.summary(), "roofline": roof}
+    if "cpu" in res:
+        e["cpu_baseline"] = res["cpu"]
+    return e
+
+
+def mixed_entry(res, fp8, tkey):
+    """A launch of both kinds: its flops and its KV bytes against both peaks,
+    and max(bytes / HBM peak, flops / MFMA peak) / time, the fraction of the
+    time the busier of the two resources needs at peak."""
+    t = res["attn_mean_s"]
+    tf, gb = res["flops"] / t / 1e12, res["kv_bytes"] / t / 1e9
+    tr = recorded_traffic(tkey)
+    e = {"workload": res["workload"], "ms_per_step": round(res["ms_per_step"], 4),
+         "config": res["wl"].summary(),
+         "roofline": {"bound": "mfma+hbm", "attn_TFLOPs": round(tf, 1),
+                      "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4), "kv_GBps": round(gb, 1),
+                      "hbm_frac": round(gb / HBM_PEAK_GBS, 4),
+                      "frac": round(max(res["kv_bytes"] / (HBM_PEAK_GBS * 1e9),
+                                        res["flops"] / (BF16_PEAK_TFLOPS * 1e12)) / t, 4),
+                      "traffic": (tr["read_bytes"] + tr["write_bytes"]) if tr else None,
+                      "traffic_read_over_algorithmic": (round(tr["read_bytes"] / res["kv_bytes"], 4)
+                                                        if tr else None),
+                      "kernel": "pa_varlen_fwd%s: %s" % ("_fp8" if fp8 else "",
+                                                         kernel_names(res, fp8)),
+                      "per_launch_flops": res["flops"], "per_launch_bytes": res["kv_bytes"],
+                      "avg_launch_us": round(t * 1e6, 2)}}
+    if "cpu" in res:
+        e["cpu_baseline"] = res["cpu"]
+    return e
+
+
+METRIC = "decode KV-read GB/s + prefill TFLOP/s, as % of MI355X roofline"
 
 
 def main():
@@ -313,64 +426,57 @@ def main():
     del calib_src, calib_dst
 
     fp8 = args.kv_dtype == "fp8"
-    head = measure(args.workload, args, dev, flush, not args.no_cpu_baseline, fp8)
-    wl = head["wl"]
-    tkey = args.workload + ("_fp8" if fp8 else "")
-    tname = ", fp8" if fp8 else ""
-    decode_like = wl.q_lens.max() * (wl.H // wl.Hkv) <= 16 or args.workload == "cascade_prefix"
-    value = head["kv_bytes"] / (head["ms_per_step"] * 1e-3) / 1e9
-    if decode_like:
-        ach = head["kv_bytes"] / head["attn_mean_s"] / 1e9
-        tr = recorded_traffic(tkey)
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4),
-                "traffic": (tr["read_bytes"] + tr["write_bytes"]) if tr else None,
-                "traffic_read_over_algorithmic": (round(tr["read_bytes"] / head["kv_bytes"], 4)
-                                                  if tr else None),
-                "kernel": "pa_varlen_fwd%s (attn_small_kernel<%d%s> + split_reduce_kernel<%d>)"
-                          % ("_fp8" if fp8 else "", wl.D, tname, wl.D),
-                "per_launch_bytes": head["kv_bytes"],
-                "avg_launch_us": round(head["attn_mean_s"] * 1e6, 2),
-                "median_launch_us": round(head["attn_median_s"] * 1e6, 2)}
-    else:
-        ach = head["flops"] / head["attn_mean_s"] / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel": "pa_varlen_fwd", "per_launch_flops": head["flops"],
-                "avg_launch_us": round(head["attn_mean_s"] * 1e6, 2)}
+    sfx = "_fp8" if fp8 else ""
+    cpu = not args.no_cpu_baseline
+    W = __import__("paged_kv_varlen_flash_amd.workloads", fromlist=["SPECS"])
+    spec = W.SPECS[args.workload]
+    head_unit = "GB/s" if (args.workload == "cascade_prefix" or all(
+        g[0] == "decode" for g in spec.groups)) and spec.fixed is None else "TFLOP/s"
+    head = measure(args.workload, args, dev, flush, head_unit if cpu else None, fp8)
+    he = entry(head, fp8, args.workload + sfx)
     line = {
-        "metric": "decode KV-read GB/s (HBM roofline fraction in roofline.frac)",
-        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "metric": METRIC,
+        "value": he["value"], "unit": he["unit"], "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": he["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "e4m3 KV cache, bf16 MFMA, fp32 softmax" if fp8 else "bf16",
         "data": ("synthetic (seeded random E4M3 cache codes, |code value| <= 15, per-KV-head "
                  "scales in [0.02, 0.1]; new tokens N(0,1) bf16 quantised by the cache write; "
                  "shuffled physical blocks)" if fp8 else
                  "synthetic (seeded N(0,1) bf16, shuffled physical blocks)"),
-        "config": dict(wl.summary(), parallelism="none (1 GPU)",
+        "config": dict(he["config"], parallelism="none (1 GPU)",
                        kv_cache_dtype="fp8_e4m3 (per-KV-head scales)" if fp8 else "bf16"),
-        "roofline": roof,
+        "roofline": he["roofline"],
     }
-    if "cpu" in head:
-        line["cpu_baseline"] = head["cpu"]
+    if "cpu_baseline" in he:
+        line["cpu_baseline"] = he["cpu_baseline"]
+    if not args.headline_only:
+        # the other half of the metric: causal prefill rows (the chunked-prefill
+        # mix's 8 prefills alone), and the mix as one launch of both kinds
+        if args.prefill_workload and args.prefill_workload != args.workload:
+            r = measure(args.prefill_workload, args, dev, flush, "TFLOP/s" if cpu else None, fp8)
+            line["prefill"] = entry(r, fp8, args.prefill_workload + sfx)
+        if args.mixed_workload and args.mixed_workload != args.workload:
+            r = measure(args.mixed_workload, args, dev, flush, "TFLOP/s" if cpu else None, fp8)
+            line["mixed"] = mixed_entry(r, fp8, args.mixed_workload + sfx)
     if args.secondary:
         sec = {}
         for name in ("chunked_prefill_mix", "chunked_prefill_mix_prefill", "prefill_causal_8k",
                      "long_decode_d256", "cascade_prefix"):
-            r = measure(name, args, dev, flush, False)
+            r = measure(name, args, dev, flush)
             w = r["wl"]
             ent = {"ms_per_step": round(r["ms_per_step"], 4),
                    "attn_avg_us": round(r["attn_mean_s"] * 1e6, 2),
+                   "kernel": kernel_names(r, False),
                    "kv_GBps": round(r["kv_bytes"] / r["attn_mean_s"] / 1e9, 1),
                    "hbm_frac": round(r["kv_bytes"] / r["attn_mean_s"] / 1e9 / HBM_PEAK_GBS, 4)}
             if name == "cascade_prefix":
                 # the host decision against both measured paths
-                from paged_kv_varlen_flash_amd import ops
                 P, use = ops.pa_cascade_decide(
                     ops.make_params(w.B, w.H, w.Hkv, w.D, w.BS, w.num_blocks,
                                     w.block_table.shape[1], w.causal, w.scale),
                     w.cu_seqlens_q, w.k_lens, w.block_table)
-                one = measure(name, args, dev, flush, False, single_pass=True)
+                one = measure(name, args, dev, flush, single_pass=True)
                 ent["single_pass_attn_avg_us"] = round(one["attn_mean_s"] * 1e6, 2)
                 ent["cascade_decision"] = {"common_prefix_len": P, "use_cascade": use}
             if name.startswith("chunked_prefill_mix") or name.startswith("prefill_"):
@@ -380,29 +486,25 @@ def main():
         if not fp8:
             # the decision on a longer shared prefix (64 requests x 16384 shared
             # tokens): both paths measured next to it
-            from paged_kv_varlen_flash_amd import ops, workloads as W
-            spec = W.Spec(name="cascade_prefix_16k", num_heads=32, num_kv_heads=8, head_size=128,
-                          block_size=16, causal=True, seed=1006, groups=(("decode", 64, 64, 512),),
-                          shared_prefix=16384)
-            W.SPECS[spec.name] = spec
-            w = W.make(spec.name, materialise=False)
+            w = W.make("cascade_prefix_16k", materialise=False)
             P, use = ops.pa_cascade_decide(
                 ops.make_params(w.B, w.H, w.Hkv, w.D, w.BS, w.num_blocks, w.block_table.shape[1],
                                 w.causal, w.scale), w.cu_seqlens_q, w.k_lens, w.block_table)
-            casc = measure(spec.name, args, dev, flush, False)
-            one = measure(spec.name, args, dev, flush, False, single_pass=True)
-            sec[spec.name] = {"attn_avg_us": round(casc["attn_mean_s"] * 1e6, 2),
-                              "single_pass_attn_avg_us": round(one["attn_mean_s"] * 1e6, 2),
-                              "cascade_decision": {"common_prefix_len": P, "use_cascade": use}}
+            casc = measure("cascade_prefix_16k", args, dev, flush)
+            one = measure("cascade_prefix_16k", args, dev, flush, single_pass=True)
+            sec["cascade_prefix_16k"] = {"attn_avg_us": round(casc["attn_mean_s"] * 1e6, 2),
+                                         "single_pass_attn_avg_us": round(one["attn_mean_s"] * 1e6, 2),
+                                         "cascade_decision": {"common_prefix_len": P,
+                                                              "use_cascade": use}}
         if not fp8:
             # decode with a 1024-key sliding window and per-head sinks
-            r = measure("decode_llama8b", args, dev, flush, False, window=1024, sinks=True)
+            r = measure("decode_llama8b", args, dev, flush, window=1024, sinks=True)
             sec["decode_llama8b_window1024_sinks"] = {
                 "attn_avg_us": round(r["attn_mean_s"] * 1e6, 2),
                 "kv_GBps": round(r["kv_bytes"] / r["attn_mean_s"] / 1e9, 1),
                 "hbm_frac": round(r["kv_bytes"] / r["attn_mean_s"] / 1e9 / HBM_PEAK_GBS, 4)}
         if not fp8:
-            r = measure("decode_llama8b", args, dev, flush, False, fp8=True)
+            r = measure("decode_llama8b", args, dev, flush, fp8=True)
             sec["decode_llama8b_fp8"] = {
                 "ms_per_step": round(r["ms_per_step"], 4),
                 "attn_avg_us": round(r["attn_mean_s"] * 1e6, 2),

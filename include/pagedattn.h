@@ -45,8 +45,9 @@ typedef enum {
 /* Static string naming a status code. */
 const char* pa_status_str(pa_status s);
 
-/* Library version, (major << 16) | minor.  Major 4 added kv_cache_fp8 to
- * pa_attn_params (the work list is unchanged, version 3).  Major 3: tiled
+/* Library version, (major << 16) | minor.  Major 5 added num_cus to
+ * pa_attn_params (plans for 256 compute units are unchanged).  Major 4 added
+ * kv_cache_fp8 to pa_attn_params (the work list is unchanged, version 3).  Major 3: tiled
  * work items of up to PA_TILED_ROWS_WIDE rows, reported in
  * pa_plan_info.tiled_rows (work-list version 3).  Major 2 added the sliding window to pa_attn_params and the
  * plan info, and the sequence's first token to the reduce items. */
@@ -90,6 +91,13 @@ typedef struct {
                                smaller cache.  A plan is valid with either
                                cache; only its split count differs.  Other
                                values: PA_ERR_INVALID_ARGUMENT */
+  int32_t num_cus;          /* compute units the planner schedules for (read
+                               by the planner only): 0 means
+                               PA_PLAN_TARGET_CUS, one whole MI355X; a
+                               partitioned or smaller device passes its own
+                               count (the binding reads it from the device).
+                               Negative or above 65536:
+                               PA_ERR_INVALID_ARGUMENT */
 } pa_attn_params;
 
 /* ------------------------------------------------------------------------
@@ -102,7 +110,8 @@ typedef struct {
  * (cu[0] == 0, non-decreasing) and seqused_k [B] (0 <= Lk <=
  * max_blocks_per_seq * block_size).
  *   force_splits     0: the planner chooses how many KV splits each work unit
- *                    gets (for PA_PLAN_TARGET_CUS compute units);
+ *                    gets (for p->num_cus compute units, PA_PLAN_TARGET_CUS
+ *                    when that is 0);
  *                    n >= 1: every unit is split into n ranges (ranges
  *                    shorter than one key tile are merged) -- for tests of
  *                    the split-KV reduction
@@ -217,8 +226,9 @@ pa_status pa_cascade_decide(const pa_attn_params* p, const int32_t* host_cu_seql
  *                     in place
  *   slot_mapping      device int64 [num_tokens]; token t goes to block
  *                     slot / block_size, offset slot % block_size; a negative
- *                     slot skips the token.  Slots must be < num_blocks *
- *                     block_size and distinct (not checked on the device).
+ *                     slot skips the token, and so does a slot >= num_blocks
+ *                     * block_size (the kernel never writes outside the
+ *                     cache).  Slots must be distinct (not checked).
  * Bit copy: the written bits equal the input bits.
  * num_tokens == 0 launches nothing and returns PA_OK.
  * ------------------------------------------------------------------------ */
@@ -245,7 +255,10 @@ pa_status pa_reshape_and_cache(const void* key, const void* value,
  *   seqused_k         device int32 [B]
  *   block_table       device int32 [B, max_blocks_per_seq]; entries at
  *                     index < ceil(seqused_k[b] / BS) must be in [0, NB);
- *                     the rest are never read
+ *                     the rest are never read.  An entry outside [0, NB)
+ *                     is not followed: its keys and values read as zeros
+ *                     (no access outside the cache; the result for that
+ *                     sequence is then meaningless)
  *   num_tokens        cu_seqlens_q[B]
  *   out               device bf16 [num_tokens, H, D]; every element is written
  *   lse               device fp32 [num_tokens, H] (natural log), or NULL
@@ -352,7 +365,12 @@ pa_status pa_varlen_fwd_ex(const pa_attn_params* p, const pa_plan_info* plan,
  *
  *   out, prefix_out, suffix_out   device bf16 [num_tokens, num_heads, head_size]
  *                                 (out may alias either input)
- *   out_lse                       device fp32 [num_tokens, num_heads] or NULL
+ *   out_lse                       device fp32 [num_tokens, num_heads] or NULL;
+ *                                 it must not alias prefix_lse or suffix_lse
+ *                                 (PA_ERR_INVALID_ARGUMENT): the threads of
+ *                                 one row read both weights before any of
+ *                                 them writes, and that order is not kept
+ *                                 across a row's threads
  *   prefix_lse, suffix_lse        device fp32 [num_tokens, num_heads]
  * head_size must be a multiple of 8 and at most 512.
  * ------------------------------------------------------------------------ */

@@ -32,11 +32,14 @@ def _run(cmd, verbose):
         raise RuntimeError("hipcc failed: " + " ".join(cmd))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libpagedattn.so; returns its path."""
-    objdir = os.path.join(HERE, "_build")
+def build(verbose: bool = False, out: str = LIB, host_flags=()) -> str:
+    """Compile every source into libpagedattn.so (at `out`); returns its path.
+    host_flags: extra flags for the host half of every source only (each is
+    passed after -Xarch_host, so the device code is unchanged)."""
+    objdir = os.path.join(HERE, "_build") if out == LIB else os.path.dirname(out)
     os.makedirs(objdir, exist_ok=True)
-    common = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    xhost = [f for flag in host_flags for f in ("-Xarch_host", flag)]
+    common = xhost + [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
               # packed fp32 VALU ops stay off: hipcc would otherwise form them
               # from plain float code (the host pass warns it does not know the
               # feature; that warning is harmless)
@@ -47,10 +50,11 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         _run([hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + common, verbose)
         objs.append(obj)
-    tmp = LIB + ".tmp"
-    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    tmp = out + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + xhost + objs,
+         verbose)
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -212,6 +212,7 @@ struct AttnArgs {
   float* part_lse;
   int64_t plane;      // elements in one cache plane (NB*BS*Hkv*D)
   int H, Hkv, G, BS, MB, bt_stride, causal;
+  int NB;             // physical blocks: a block-table entry outside [0, NB) reads as zeros
   int bs_log2;        // log2(BS) when BS is a power of two, else -1
   float scale_log2;   // scale * log2(e)
   const float* k_scale;   // E4M3 cache: per-KV-head dequantisation scales
@@ -235,47 +236,54 @@ __device__ __forceinline__ float add_sink(float sink_l2, float& m, float& l, flo
   return a;
 }
 
+// 64-bit load of a wave-uniform value (the token's slot) as a scalar load
+__device__ __forceinline__ int64_t ld_uniform64(const int64_t* p) {
+  typedef const __attribute__((address_space(4))) int64_t* const_i64_ptr;
+  return *(const_i64_ptr)(reinterpret_cast<uintptr_t>(p));
+}
+
 // ---------------------------------------------------------------------------
-// reshape_and_cache: one thread per 16-byte chunk; consecutive threads take
-// consecutive chunks of one token's K (then V) row.
+// reshape_and_cache: one wave per token (four tokens per workgroup).  The
+// token's slot is one scalar load; the lanes walk its K row and its V row in
+// 16-byte chunks, two chunks per plane in flight per lane, so no index needs
+// a division.  Slots outside [0, num_slots) are skipped.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const uint16_t* __restrict__ key, const uint16_t* __restrict__ value, int64_t key_stride,
     int64_t value_stride, uint16_t* __restrict__ cache, const int64_t* __restrict__ slot_mapping,
-    int64_t total_chunks, int32_t chunks_per_row, int64_t row_elems, int64_t plane) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= total_chunks) return;
-  const int64_t tw = gid / chunks_per_row;      // token * 2 + which
-  const int32_t c = (int32_t)(gid - tw * chunks_per_row);
-  const int64_t t = tw >> 1;
-  const int which = (int)(tw & 1);
-  const int64_t slot = slot_mapping[t];
-  if (slot < 0) return;
-  const uint16_t* src = which ? value + t * value_stride : key + t * key_stride;
-  uint16_t* dst = cache + (which ? plane : 0) + slot * row_elems;
-  reinterpret_cast<uint4*>(dst)[c] = reinterpret_cast<const uint4*>(src)[c];
+    int32_t num_tokens, int32_t cpr, int64_t row_elems, int64_t plane, int64_t num_slots) {
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (t >= num_tokens) return;
+  const int64_t slot = ld_uniform64(slot_mapping + t);
+  if (slot < 0 || slot >= num_slots) return;
+  const int lane = threadIdx.x & 63;
+  const uint4* ks = reinterpret_cast<const uint4*>(key + (int64_t)t * key_stride);
+  const uint4* vs = reinterpret_cast<const uint4*>(value + (int64_t)t * value_stride);
+  uint4* kd = reinterpret_cast<uint4*>(cache + slot * row_elems);
+  uint4* vd = reinterpret_cast<uint4*>(cache + plane + slot * row_elems);
+  for (int c = lane; c < cpr; c += 128) {
+    const bool two = c + 64 < cpr;
+    const uint4 k0 = ks[c], v0 = vs[c];
+    uint4 k1 = k0, v1 = v0;
+    if (two) {
+      k1 = ks[c + 64];
+      v1 = vs[c + 64];
+    }
+    kd[c] = k0;
+    vd[c] = v0;
+    if (two) {
+      kd[c + 64] = k1;
+      vd[c + 64] = v1;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
-// reshape_and_cache into an E4M3 cache: one thread per 16 output bytes (16
-// elements of one token's K or V row); code = E4M3(x / scale[kv head]), the
-// division in IEEE fp32.
+// reshape_and_cache into an E4M3 cache: one wave per token, as above; a lane
+// turns 16 elements of the K (V) row into 16 output bytes, code =
+// E4M3(x / scale[kv head]), the division in IEEE fp32.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
-    const uint16_t* __restrict__ key, const uint16_t* __restrict__ value, int64_t key_stride,
-    int64_t value_stride, uint8_t* __restrict__ cache, const int64_t* __restrict__ slot_mapping,
-    const float* __restrict__ k_scale, const float* __restrict__ v_scale, int64_t total_chunks,
-    int32_t chunks_per_row, int32_t chunks_per_head, int64_t row_elems, int64_t plane) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= total_chunks) return;
-  const int64_t tw = gid / chunks_per_row;      // token * 2 + which
-  const int32_t c = (int32_t)(gid - tw * chunks_per_row);
-  const int64_t t = tw >> 1;
-  const int which = (int)(tw & 1);
-  const int64_t slot = slot_mapping[t];
-  if (slot < 0) return;
-  const uint16_t* src = (which ? value + t * value_stride : key + t * key_stride) + c * 16;
-  const float sc = (which ? v_scale : k_scale)[c / chunks_per_head];
+__device__ __forceinline__ uint4 e4m3x16_from_bf16(const uint16_t* src, float sc) {
   const uint4 w0 = reinterpret_cast<const uint4*>(src)[0];
   const uint4 w1 = reinterpret_cast<const uint4*>(src)[1];
   const uint32_t in[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
@@ -285,8 +293,28 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
     const uint32_t bits = (k & 1) ? (in[k >> 1] & 0xffff0000u) : (in[k >> 1] << 16);
     o[k >> 2] |= f32_to_e4m3(__builtin_bit_cast(float, bits) / sc) << (8 * (k & 3));
   }
-  uint8_t* dst = cache + (which ? plane : 0) + slot * row_elems + (int64_t)c * 16;
-  *reinterpret_cast<uint4*>(dst) = uint4{o[0], o[1], o[2], o[3]};
+  return uint4{o[0], o[1], o[2], o[3]};
+}
+
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
+    const uint16_t* __restrict__ key, const uint16_t* __restrict__ value, int64_t key_stride,
+    int64_t value_stride, uint8_t* __restrict__ cache, const int64_t* __restrict__ slot_mapping,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale, int32_t num_tokens,
+    int32_t cpr, int32_t chunks_per_head, int64_t row_elems, int64_t plane, int64_t num_slots) {
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (t >= num_tokens) return;
+  const int64_t slot = ld_uniform64(slot_mapping + t);
+  if (slot < 0 || slot >= num_slots) return;
+  const int lane = threadIdx.x & 63;
+  const uint16_t* ks = key + (int64_t)t * key_stride;
+  const uint16_t* vs = value + (int64_t)t * value_stride;
+  uint4* kd = reinterpret_cast<uint4*>(cache + slot * row_elems);
+  uint4* vd = reinterpret_cast<uint4*>(cache + plane + slot * row_elems);
+  for (int c = lane; c < cpr; c += 64) {
+    const int h = c / chunks_per_head;
+    kd[c] = e4m3x16_from_bf16(ks + c * 16, k_scale[h]);
+    vd[c] = e4m3x16_from_bf16(vs + c * 16, v_scale[h]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -432,9 +460,11 @@ __device__ __forceinline__ void small_body(const AttnArgs& a, const int32_t* ite
     if (kb < kv1) {
       const int blk = (a.bs_log2 >= 0) ? (kb >> a.bs_log2) : (kb / a.BS);
       const int phys = ld_uniform(btrow + blk);
-      const int valid = min(16, kv1 - kb);
-      boff = ((int64_t)phys * a.BS + (kb - blk * a.BS)) * row_elems * ES + kv_bytes;
-      nrec = (valid - 1) * (int)(row_elems * ES) + D * ES;
+      if ((unsigned)phys < (unsigned)a.NB) {
+        const int valid = min(16, kv1 - kb);
+        boff = ((int64_t)phys * a.BS + (kb - blk * a.BS)) * row_elems * ES + kv_bytes;
+        nrec = (valid - 1) * (int)(row_elems * ES) + D * ES;
+      }
     }
     const __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(cache_b + boff), 0, nrec, 0x00020000);
@@ -737,8 +767,10 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
         if (kb < kv1) {
           const int blk = (bs_log2 >= 0) ? (kb >> bs_log2) : (kb / a.BS);
           const int phys = ld_uniform(btrow + blk);
-          boff = ((int64_t)phys * a.BS + (kb - blk * a.BS)) * row_elems * 2;
-          nrec = (min(KSTEP, kv1 - kb) - 1) * row_bytes + D * 2;
+          if ((unsigned)phys < (unsigned)a.NB) {
+            boff = ((int64_t)phys * a.BS + (kb - blk * a.BS)) * row_elems * 2;
+            nrec = (min(KSTEP, kv1 - kb) - 1) * row_bytes + D * 2;
+          }
         }
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t*>(cache_b + boff), 0, nrec, 0x00020000);
@@ -751,7 +783,8 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int key = j0 + lkey + KSTEP * i;
-        if (key < kv1) {
+        const int phys = (key < kv1) ? btrow[(bs_log2 >= 0) ? (key >> bs_log2) : (key / a.BS)] : -1;
+        if ((unsigned)phys < (unsigned)a.NB) {
           int blk, off;
           if (bs_log2 >= 0) {
             blk = key >> bs_log2;
@@ -760,7 +793,7 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
             blk = key / a.BS;
             off = key - blk * a.BS;
           }
-          const uint16_t* p = cbase + ((int64_t)btrow[blk] * a.BS + off) * row_elems;
+          const uint16_t* p = cbase + ((int64_t)phys * a.BS + off) * row_elems;
           kr[i] = ld16(p);
           vr[i] = ld16(p + a.plane);
         } else {
@@ -805,7 +838,7 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
         phys = ph[c] ^ ((ph[c] ^ ph[c + 1]) & m);
         bse = b16[c] ^ ((b16[c] ^ b16[c + 1]) & m);
       }
-      if (j0 + kk < kv1) {
+      if (j0 + kk < kv1 && (unsigned)phys < (unsigned)a.NB) {
         const uint16_t* p = cbase + ((int64_t)phys * a.BS + bse + (kk & 15)) * row_elems;
         kr[i] = ld16(p);
         vr[i] = ld16(p + a.plane);
@@ -846,7 +879,7 @@ __device__ __forceinline__ void tiled_body(const AttnArgs& a, const int32_t* ite
         ph = (grp == g4) ? phys16[g4] : ph;
         bs = (grp == g4) ? base16[g4] : bs;
       }
-      if (j0 + kk < kv1) {
+      if (j0 + kk < kv1 && (unsigned)ph < (unsigned)a.NB) {
         const uint8_t* p8 = cbase8 + ((int64_t)ph * a.BS + bs + (kk & 15)) * row_elems;
         k8[i] = *reinterpret_cast<const u32x4_t*>(p8);
         v8[i] = *reinterpret_cast<const u32x4_t*>(p8 + a.plane);
@@ -1185,18 +1218,22 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Two-way merge of (out, lse) partial states; one thread per 8 elements.
+// Two-way merge of (out, lse) partial states.  A row of D elements is
+// cpr = D/8 chunks of 8; a wave holds 64 >> p2 rows of 1 << p2 lanes (the
+// smallest power of two >= cpr, cpr <= 64), so a lane's row and chunk come
+// from shifts.  out may alias po or so: each lane reads its 8 elements before
+// writing them.  out_lse does not alias pl or sl (the entry point checks).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void merge_states_kernel(
     uint16_t* out, float* __restrict__ out_lse, const uint16_t* po, const float* __restrict__ pl,
-    const uint16_t* so, const float* __restrict__ sl, int64_t rows, int32_t chunks_per_row) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t row = gid / chunks_per_row;
-  if (row >= rows) return;
-  const int c = (int)(gid - row * chunks_per_row);
+    const uint16_t* so, const float* __restrict__ sl, int64_t rows, int32_t cpr, int32_t p2) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane & ((1 << p2) - 1);
+  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 >> p2) + (lane >> p2);
+  if (row >= rows || c >= cpr) return;
   const float lp = pl[row], ls = sl[row];
   const float M = fmaxf(lp, ls);
-  const int64_t off = row * chunks_per_row * 8 + c * 8;
+  const int64_t off = row * cpr * 8 + c * 8;
   const uint4 wp = *reinterpret_cast<const uint4*>(po + off);
   const uint4 ws = *reinterpret_cast<const uint4*>(so + off);
   float res[8];
@@ -1283,13 +1320,11 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, int64_t key_r
     return PA_ERR_INVALID_ARGUMENT;
   const int64_t plane = (int64_t)num_blocks * block_size * row;
   const int32_t cpr = (int32_t)(row / 8);
-  const int64_t total = (int64_t)num_tokens * 2 * cpr;
-  const int64_t blocks = (total + 255) / 256;
-  if (blocks > INT32_MAX) return PA_ERR_INVALID_ARGUMENT;
-  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
+  const uint32_t blocks = (uint32_t)((num_tokens + 3) / 4);
+  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(blocks), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),
                      key_row_stride, value_row_stride, static_cast<uint16_t*>(kv_cache),
-                     slot_mapping, total, cpr, row, plane);
+                     slot_mapping, num_tokens, cpr, row, plane, (int64_t)num_blocks * block_size);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -1314,13 +1349,12 @@ pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, int64_t k
     return PA_ERR_INVALID_ARGUMENT;
   const int64_t plane = (int64_t)num_blocks * block_size * row;   // bytes
   const int32_t cpr = (int32_t)(row / 16);
-  const int64_t total = (int64_t)num_tokens * 2 * cpr;
-  const int64_t blocks = (total + 255) / 256;
-  if (blocks > INT32_MAX) return PA_ERR_INVALID_ARGUMENT;
-  hipLaunchKernelGGL(reshape_and_cache_fp8_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
+  const uint32_t blocks = (uint32_t)((num_tokens + 3) / 4);
+  hipLaunchKernelGGL(reshape_and_cache_fp8_kernel, dim3(blocks), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),
                      key_row_stride, value_row_stride, static_cast<uint8_t*>(kv_cache),
-                     slot_mapping, k_scale, v_scale, total, cpr, head_size / 16, row, plane);
+                     slot_mapping, k_scale, v_scale, num_tokens, cpr, head_size / 16, row, plane,
+                     (int64_t)num_blocks * block_size);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -1386,6 +1420,7 @@ pa_status varlen_fwd(const pa_attn_params* p, const pa_plan_info* plan, const in
                                                     (o_bytes + 255) / 256 * 256)
                          : nullptr;
   a.plane = (int64_t)p->num_blocks * p->block_size * p->num_kv_heads * p->head_size;
+  a.NB = p->num_blocks;
   a.H = p->num_heads;
   a.Hkv = p->num_kv_heads;
   a.G = p->num_heads / p->num_kv_heads;
@@ -1462,12 +1497,21 @@ pa_status pa_merge_attn_states(void* out, float* out_lse, const void* prefix_out
   if (!aligned(out, 16) || !aligned(prefix_out, 16) || !aligned(suffix_out, 16))
     return PA_ERR_INVALID_ARGUMENT;
   const int64_t rows = (int64_t)num_tokens * num_heads;
+  // out_lse must not overlap either input lse (the lanes of one row read the
+  // inputs and one of them writes out_lse, in no fixed order)
+  if (out_lse) {
+    auto overlaps = [rows](const float* x, const float* y) { return x < y + rows && y < x + rows; };
+    if (overlaps(out_lse, prefix_lse) || overlaps(out_lse, suffix_lse)) return PA_ERR_INVALID_ARGUMENT;
+  }
   const int32_t cpr = head_size / 8;
-  const int64_t blocks = (rows * cpr + 255) / 256;
+  int32_t p2 = 0;
+  while ((1 << p2) < cpr) ++p2;
+  const int64_t rows_per_block = 4 * (64 >> p2);
+  const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
   if (blocks > INT32_MAX) return PA_ERR_INVALID_ARGUMENT;
   hipLaunchKernelGGL(merge_states_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
                      static_cast<uint16_t*>(out), out_lse, static_cast<const uint16_t*>(prefix_out),
-                     prefix_lse, static_cast<const uint16_t*>(suffix_out), suffix_lse, rows, cpr);
+                     prefix_lse, static_cast<const uint16_t*>(suffix_out), suffix_lse, rows, cpr, p2);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -41,6 +41,7 @@ pa_status check_params(const pa_attn_params* p) {
   if ((int64_t)p->max_blocks_per_seq * p->block_size > INT32_MAX / 2) return PA_ERR_INVALID_ARGUMENT;
   if (p->causal != 0 && p->causal != 1) return PA_ERR_INVALID_ARGUMENT;
   if (p->kv_cache_fp8 != 0 && p->kv_cache_fp8 != 1) return PA_ERR_INVALID_ARGUMENT;
+  if (p->num_cus < 0 || p->num_cus > 65536) return PA_ERR_INVALID_ARGUMENT;
   // a sliding window is the causal band of its last W keys
   if (p->sliding_window < 0 || (p->sliding_window > 0 && !p->causal)) return PA_ERR_INVALID_ARGUMENT;
   // a softmax scale is positive (the kernels take row maxima on unscaled scores)
@@ -207,7 +208,8 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
     if (u.small) { small_keys += u.kv_end - u.kv_begin; ++n_small; }
     else { tiled_keys += u.kv_end - u.kv_begin; ++n_tiled; }
   }
-  const int64_t target = PA_PLAN_TARGET_CUS;
+  // compute units to fill: the caller's device, or one whole MI355X
+  const int64_t target = p->num_cus > 0 ? p->num_cus : PA_PLAN_TARGET_CUS;
   int64_t tiled_chunk = 0;
   // tiled rows (bound by the matrix cores): split only when there are too
   // few blocks to fill the chip; cuts fall on whole key tiles
@@ -382,7 +384,12 @@ extern "C" {
 const int32_t pa_supported_head_sizes[PA_NUM_HEAD_SIZES] = {64, 128, 256};
 
 const char* pa_status_str(pa_status s) {
-  switch (s) {
+  // callers may pass any int; it is read as one (loading a C++ enum whose
+  // value lies outside its enumerators' range is undefined behaviour)
+  static_assert(sizeof(pa_status) == sizeof(int32_t), "pa_status is passed as an int");
+  int32_t code;
+  std::memcpy(&code, &s, sizeof code);
+  switch (code) {
     case PA_OK: return "PA_OK";
     case PA_ERR_INVALID_ARGUMENT: return "PA_ERR_INVALID_ARGUMENT";
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
@@ -392,7 +399,7 @@ const char* pa_status_str(pa_status s) {
   return "PA_ERR_UNKNOWN";
 }
 
-int32_t pa_version(void) { return (4 << 16) | 0; }
+int32_t pa_version(void) { return (5 << 16) | 0; }
 
 pa_status pa_plan_varlen(const pa_attn_params* p, const int32_t* host_cu_seqlens_q,
                          const int32_t* host_seqused_k, int32_t force_splits,

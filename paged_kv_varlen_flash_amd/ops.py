@@ -20,7 +20,9 @@ from typing import Optional, Tuple
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+# PA_LIBRARY names another build of the same library (for instance one whose
+# host code is compiled with sanitizers); by default the in-tree build
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_HERE, "libpagedattn.so")
 
 PA_OK = 0
 PA_ERR_INVALID_ARGUMENT = 1
@@ -52,7 +54,8 @@ class AttnParams(ctypes.Structure):
                 ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
                 ("max_blocks_per_seq", ctypes.c_int32), ("block_table_stride", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("sliding_window", ctypes.c_int32), ("kv_cache_fp8", ctypes.c_int32)]
+                ("sliding_window", ctypes.c_int32), ("kv_cache_fp8", ctypes.c_int32),
+                ("num_cus", ctypes.c_int32)]
 
     def __repr__(self):
         return "AttnParams(" + ", ".join(f"{k}={getattr(self, k)}" for k, _ in self._fields_) + ")"
@@ -155,11 +158,19 @@ def _ptr_i32(a: Optional[np.ndarray]):
 
 def make_params(batch, num_heads, num_kv_heads, head_size, block_size, num_blocks,
                 max_blocks_per_seq, causal, scale, block_table_stride=0,
-                sliding_window=0, kv_cache_fp8=False) -> AttnParams:
+                sliding_window=0, kv_cache_fp8=False, num_cus=0) -> AttnParams:
+    """num_cus: compute units the planner fills (0: PA_PLAN_TARGET_CUS)."""
     return AttnParams(int(batch), int(num_heads), int(num_kv_heads), int(head_size),
                       int(block_size), int(num_blocks), int(max_blocks_per_seq),
                       int(block_table_stride), int(bool(causal)), float(np.float32(scale)),
-                      int(sliding_window), int(bool(kv_cache_fp8)))
+                      int(sliding_window), int(bool(kv_cache_fp8)), int(num_cus))
+
+
+def device_cus(device=None) -> int:
+    """Compute units of a GPU, for AttnParams.num_cus."""
+    import torch
+    return int(torch.cuda.get_device_properties(device or torch.cuda.current_device())
+               .multi_processor_count)
 
 
 # --------------------------------------------------------------------------
@@ -251,9 +262,52 @@ def pa_reshape_and_cache(key, value, kv_cache, slot_mapping, stream=None):
     _check(st, "pa_reshape_and_cache")
 
 
+def _shape(t):
+    return tuple(t.shape)
+
+
+def check_fwd_args(params: AttnParams, plan: PlanInfo, worklist, q, kv_cache, cu_seqlens_q,
+                   seqused_k, block_table, out, lse, fp8=False):
+    """Host-side shape, stride and dtype checks of a forward call against its
+    params and plan, before any launch: the kernels index these buffers with
+    the shapes the params state, so a mismatch would read or write outside
+    an allocation.  Raises ValueError."""
+    T, H, D = int(plan.num_tokens), int(params.num_heads), int(params.head_size)
+    B, Hkv = int(params.batch), int(params.num_kv_heads)
+    for name, t in (("q", q), ("out", out)):
+        if t is None or t.shape != (T, H, D) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [{T}, {H}, {D}] tensor "
+                             f"(plan.num_tokens, num_heads, head_size), got "
+                             f"{None if t is None else _shape(t)}")
+    if lse is not None and (lse.shape != (T, H) or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous [{T}, {H}] tensor, got {_shape(lse)}")
+    want_kv = (2, int(params.num_blocks), int(params.block_size), Hkv, D)
+    if kv_cache.shape != want_kv or not kv_cache.is_contiguous():
+        raise ValueError(f"kv_cache must be a contiguous {want_kv} tensor, got {_shape(kv_cache)}")
+    if kv_cache.element_size() != (1 if fp8 else 2):
+        raise ValueError("kv_cache element size does not match the cache format")
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_q.numel() < B + 1 or not cu_seqlens_q.is_contiguous():
+        raise ValueError(f"cu_seqlens_q must be a contiguous int32 vector of {B + 1} entries")
+    if seqused_k.dim() != 1 or seqused_k.numel() < B or not seqused_k.is_contiguous():
+        raise ValueError(f"seqused_k must be a contiguous int32 vector of {B} entries")
+    stride = int(params.block_table_stride) or int(params.max_blocks_per_seq)
+    if B > 0 and (block_table.dim() != 2 or block_table.shape[0] < B
+                  or block_table.shape[1] < params.max_blocks_per_seq
+                  or block_table.stride(1) != 1
+                  or (block_table.shape[0] > 1 and block_table.stride(0) != stride)):
+        raise ValueError(f"block_table must be [>= {B}, >= {params.max_blocks_per_seq}] with row "
+                         f"stride {stride}, got {_shape(block_table)} strides "
+                         f"{tuple(block_table.stride())}")
+    if worklist.numel() * worklist.element_size() < plan.worklist_bytes or \
+            not worklist.is_contiguous():
+        raise ValueError("worklist is smaller than plan.worklist_bytes")
+
+
 def pa_varlen_fwd(params: AttnParams, plan: PlanInfo, worklist, q, kv_cache, cu_seqlens_q,
                   seqused_k, block_table, out, lse=None, workspace=None, stream=None):
     import torch
+    check_fwd_args(params, plan, worklist, q, kv_cache, cu_seqlens_q, seqused_k, block_table,
+                   out, lse)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().pa_varlen_fwd(
         ctypes.byref(params), ctypes.byref(plan), _dev(worklist, "worklist", torch.int32),
@@ -290,6 +344,10 @@ def pa_varlen_fwd_fp8(params: AttnParams, plan: PlanInfo, worklist, q, kv_cache,
                       seqused_k, block_table, k_scale, v_scale, out, lse=None, workspace=None,
                       stream=None):
     import torch
+    check_fwd_args(params, plan, worklist, q, kv_cache, cu_seqlens_q, seqused_k, block_table,
+                   out, lse, fp8=True)
+    if k_scale.numel() != params.num_kv_heads or v_scale.numel() != params.num_kv_heads:
+        raise ValueError("k_scale and v_scale need one entry per KV head")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().pa_varlen_fwd_fp8(
         ctypes.byref(params), ctypes.byref(plan), _dev(worklist, "worklist", torch.int32),
@@ -309,6 +367,13 @@ def pa_varlen_fwd_ex(params: AttnParams, plan: PlanInfo, worklist, q, kv_cache, 
     s_aux: None or fp32 [H] sink logits."""
     import torch
     fp8 = k_scale is not None or v_scale is not None
+    check_fwd_args(params, plan, worklist, q, kv_cache, cu_seqlens_q, seqused_k, block_table,
+                   out, lse, fp8=fp8)
+    if fp8 and (k_scale is None or v_scale is None or k_scale.numel() != params.num_kv_heads
+                or v_scale.numel() != params.num_kv_heads):
+        raise ValueError("k_scale and v_scale need one entry per KV head")
+    if s_aux is not None and s_aux.numel() != params.num_heads:
+        raise ValueError("s_aux needs one entry per query head")
     opt = FwdOptions(PA_KV_E4M3 if fp8 else PA_KV_BF16,
                      _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
                      _dev(s_aux, "s_aux", torch.float32))
@@ -368,7 +433,7 @@ def plan_varlen(q_shape, kv_cache_shape, block_table_shape, host_cu_seqlens_q, h
         raise ValueError("head size of q and kv_cache differ")
     B, MB = block_table_shape
     p = make_params(B, H, Hkv, D, BS, NB, MB, causal, scale, block_table_stride, sliding_window,
-                    kv_cache_fp8)
+                    kv_cache_fp8, num_cus=device_cus())
     return VarlenPlan(p, host_cu_seqlens_q, host_seqused_k, force_splits)
 
 
@@ -404,7 +469,7 @@ class CascadePlan:
         T, H, D = q_shape
         _, NB, BS, Hkv, _ = kv_cache_shape
         B, MB = block_table_shape
-        full = make_params(B, H, Hkv, D, BS, NB, MB, True, scale)
+        full = make_params(B, H, Hkv, D, BS, NB, MB, True, scale, num_cus=device_cus())
         pp, sp, pcu, psk, ssk, col0 = pa_cascade_split(full, common_prefix_len,
                                                        host_cu_seqlens_q, host_seqused_k)
         self.prefix = VarlenPlan(pp, pcu, psk, force_splits)

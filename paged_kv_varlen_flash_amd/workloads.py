@@ -104,6 +104,11 @@ SPECS = {
         causal=True, seed=1004, groups=(("decode", 32, 64, 512),), shared_prefix=2048,
         description="32 decode reqs sharing a 2048-token prefix + private suffix "
                     "U[64,512]; H=32 Hkv=8 D=128 BS=16"),
+    "cascade_prefix_16k": Spec(
+        name="cascade_prefix_16k", num_heads=32, num_kv_heads=8, head_size=128, block_size=16,
+        causal=True, seed=1006, groups=(("decode", 64, 64, 512),), shared_prefix=16384,
+        description="64 decode reqs sharing a 16384-token prefix + private suffix U[64,512]; "
+                    "H=32 Hkv=8 D=128 BS=16 (the cascade decision's other side)"),
     "long_decode_d256": Spec(
         name="long_decode_d256", num_heads=16, num_kv_heads=2, head_size=256, block_size=64,
         causal=True, seed=1005, groups=(("decode", 16, 32768, 131072),),

@@ -43,7 +43,7 @@ def test_status_strings_and_version(L):
     assert ops.status_str(0) == "PA_OK"
     assert ops.status_str(3) == "PA_ERR_WORKSPACE_TOO_SMALL"
     assert ops.status_str(99) == "PA_ERR_UNKNOWN"
-    assert L.pa_version() >> 16 == 4              # pa_attn_params.kv_cache_fp8
+    assert L.pa_version() >> 16 == 5              # pa_attn_params.num_cus
     assert ops.supported_head_sizes() == [64, 128, 256]
 
 
@@ -200,6 +200,18 @@ def test_merge_validation(L):
     assert f(P(0x1000), None, P(0), P(0x3000), P(0x4000), P(0x5000), 4, 2, 64, None) == E
     assert f(P(0x1008), None, P(0x2000), P(0x3000), P(0x4000), P(0x5000), 4, 2, 64, None) == E
     assert f(P(0), None, P(0), P(0), P(0), P(0), 0, 2, 64, None) == ops.PA_OK
+
+
+def test_merge_rejects_lse_aliasing(L):
+    """out_lse may not overlap prefix_lse or suffix_lse (rows of 4 tokens x
+    2 heads = 8 floats = 32 bytes); out may still alias either output."""
+    P = ctypes.c_void_p
+    E = ops.PA_ERR_INVALID_ARGUMENT
+    f = L.pa_merge_attn_states
+    assert f(P(0x1000), P(0x3000), P(0x1000), P(0x3000), P(0x4000), P(0x5000), 4, 2, 64, None) == E
+    assert f(P(0x1000), P(0x5000), P(0x2000), P(0x3000), P(0x4000), P(0x5000), 4, 2, 64, None) == E
+    assert f(P(0x1000), P(0x3010), P(0x2000), P(0x3000), P(0x4000), P(0x5000), 4, 2, 64, None) == E
+    assert f(P(0x1000), P(0x2ff0), P(0x2000), P(0x3000), P(0x4000), P(0x5000), 4, 2, 64, None) == E
 
 
 def test_cascade_split(L):
@@ -538,6 +550,83 @@ def test_plan_covers_sliding_window(L, seed):
                     assert k0 == pos
                     pos = k1
                 assert pos >= hi + 1 or hi < lo
+
+
+def test_num_cus(L):
+    """num_cus = 256 plans exactly as num_cus = 0 (PA_PLAN_TARGET_CUS); a
+    smaller device gets fewer, longer decode pieces; out-of-range values are
+    rejected."""
+    wl = W.make("decode_llama8b", materialise=False)
+    def plan(n):
+        p = ops.make_params(wl.B, wl.H, wl.Hkv, wl.D, wl.BS, wl.num_blocks,
+                            wl.block_table.shape[1], True, wl.scale, num_cus=n)
+        return ops.pa_plan_varlen(p, wl.cu_seqlens_q, wl.k_lens)
+    w0, i0 = plan(0)
+    w256, i256 = plan(256)
+    assert np.array_equal(w0, w256) and i0.as_dict() == i256.as_dict()
+    w32, i32 = plan(32)
+    assert i32.num_small_items < i0.num_small_items
+    check = lambda n: ops.pa_plan_varlen(
+        ops.make_params(2, 4, 2, 64, 16, 16, 6, True, 0.125, num_cus=n), CU, SK)
+    for bad in (-1, 65537):
+        with pytest.raises(ops.PaError):
+            check(bad)
+
+
+def test_binding_checks_fwd_shapes():
+    """The forward bindings check shapes, strides and sizes against the params
+    and the plan before any launch (CPU tensors: a call that passes the checks
+    stops at the device-tensor check instead, with TypeError)."""
+    import torch
+    wl = W.make("tiny_mixed")
+    T, H, D, Hkv = wl.T, wl.H, wl.D, wl.Hkv
+    p = ops.make_params(wl.B, H, Hkv, D, wl.BS, wl.num_blocks, wl.block_table.shape[1], True,
+                        wl.scale)
+    words, info = ops.pa_plan_varlen(p, wl.cu_seqlens_q, wl.k_lens)
+    good = dict(worklist=torch.from_numpy(words), q=torch.zeros(T, H, D, dtype=torch.bfloat16),
+                kv_cache=torch.zeros(2, wl.num_blocks, wl.BS, Hkv, D, dtype=torch.bfloat16),
+                cu_seqlens_q=torch.from_numpy(wl.cu_seqlens_q.astype(np.int32)),
+                seqused_k=torch.from_numpy(wl.k_lens.astype(np.int32)),
+                block_table=torch.from_numpy(wl.block_table.astype(np.int32)),
+                out=torch.zeros(T, H, D, dtype=torch.bfloat16),
+                lse=torch.zeros(T, H, dtype=torch.float32))
+
+    def call(**bad):
+        a = dict(good, **bad)
+        ops.pa_varlen_fwd(p, info, a["worklist"], a["q"], a["kv_cache"], a["cu_seqlens_q"],
+                          a["seqused_k"], a["block_table"], a["out"], a["lse"])
+
+    with pytest.raises(TypeError):        # all checks pass; CPU tensors stop here
+        call()
+    bt = good["block_table"]
+    wide = torch.zeros(bt.shape[0], bt.shape[1] + 3, dtype=torch.int32)
+    for bad in (dict(out=torch.zeros(T + 1, H, D, dtype=torch.bfloat16)),
+                dict(out=torch.zeros(T, H, D + 8, dtype=torch.bfloat16)),
+                dict(out=torch.zeros(T, D, H, dtype=torch.bfloat16).transpose(1, 2)),
+                dict(q=torch.zeros(T - 1, H, D, dtype=torch.bfloat16)),
+                dict(lse=torch.zeros(T, H + 1, dtype=torch.float32)),
+                dict(lse=torch.zeros(H, T, dtype=torch.float32).t()),
+                dict(kv_cache=torch.zeros(2, wl.num_blocks - 1, wl.BS, Hkv, D,
+                                          dtype=torch.bfloat16)),
+                dict(kv_cache=torch.zeros(2, wl.num_blocks, wl.BS, Hkv, D, dtype=torch.uint8)),
+                dict(block_table=bt[:1]),
+                dict(block_table=bt[:, :-1]),
+                dict(block_table=wide[:, :bt.shape[1]]),          # row stride differs from params
+                dict(cu_seqlens_q=good["cu_seqlens_q"][:-1]),
+                dict(seqused_k=good["seqused_k"][:1]),
+                dict(worklist=good["worklist"][:-1])):
+        with pytest.raises(ValueError):
+            call(**bad)
+    # the E4M3 entry point: the scales must cover every KV head
+    kv8 = torch.zeros(2, wl.num_blocks, wl.BS, Hkv, D, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        ops.pa_varlen_fwd_fp8(p, info, good["worklist"], good["q"], kv8, good["cu_seqlens_q"],
+                              good["seqused_k"], bt, torch.ones(Hkv - 1), torch.ones(Hkv),
+                              good["out"], good["lse"])
+    with pytest.raises(ValueError):
+        ops.pa_varlen_fwd_ex(p, info, good["worklist"], good["q"], good["kv_cache"],
+                             good["cu_seqlens_q"], good["seqused_k"], bt, good["out"],
+                             good["lse"], s_aux=torch.zeros(H + 1))
 
 
 def test_window_params_validation(L):
