@@ -211,7 +211,8 @@ def test_graph_capture_scatter_attention():
         compare(out.float().cpu().numpy(), lse.cpu().numpy(), ref_out, ref_lse, label=label)
 
     _replays(g, check, reset)
-    assert torch.equal(d["kv_cache"], cache0)
+    # bit patterns (the slack slots hold NaN sentinels)
+    assert torch.equal(d["kv_cache"].view(torch.int16), cache0.view(torch.int16))
 
 
 def test_graph_capture_cascade():
