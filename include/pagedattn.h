@@ -356,6 +356,35 @@ pa_status pa_varlen_fwd_ex(const pa_attn_params* p, const pa_plan_info* plan,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * pa_varlen_fwd_noalloc -- pa_varlen_fwd_ex for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): no workspace argument; the split-KV
+ * partials go to a scratch array compiled into the library,
+ * PA_NOALLOC_SCRATCH_BYTES on every GPU the library runs on, held until the
+ * process ends.  The call allocates nothing; its first call on a device
+ * (after all argument checks) resolves that device's scratch address once.
+ *
+ *   opt        as for pa_varlen_fwd_ex, or NULL: bf16 cache, no sinks
+ *   the other arguments are those of pa_varlen_fwd_ex (the work list is
+ *   still the caller's device copy of the plan)
+ * Calls on one GPU share its scratch, which keeps the last call's partials;
+ * nothing in it needs clearing (every partial row is written before the
+ * same call reads it), but calls that overlap on one GPU (on two streams, or
+ * in two graphs replayed concurrently) race: the caller orders them.
+ * Errors: those of pa_varlen_fwd_ex; PA_ERR_WORKSPACE_TOO_SMALL when
+ * plan->workspace_bytes > PA_NOALLOC_SCRATCH_BYTES; PA_ERR_HIP when the
+ * scratch address cannot be resolved.
+ * ------------------------------------------------------------------------ */
+#define PA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+pa_status pa_varlen_fwd_noalloc(const pa_attn_params* p, const pa_plan_info* plan,
+                                const int32_t* worklist,
+                                const void* q, const void* kv_cache,
+                                const int32_t* cu_seqlens_q, const int32_t* seqused_k,
+                                const int32_t* block_table, const pa_fwd_options* opt,
+                                int32_t num_tokens, void* out, float* lse, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * pa_merge_attn_states -- LSE-weighted merge of two partial attentions over
  * disjoint key sets (the cascade's third step, "FlashAttention 在 vLLM 中的
  * 实现分析" section 6.3, and the merge_attn_states helper of section 8.2):

@@ -30,6 +30,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "pagedattn.h"
 #include "plan_internal.h"
@@ -1362,14 +1363,38 @@ pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, int64_t k
 
 namespace {
 
-// pa_varlen_fwd and pa_varlen_fwd_fp8: fp8 selects the E4M3 cache with its
-// per-KV-head scales
+// The split-KV partials of pa_varlen_fwd_noalloc: a device array compiled
+// into the library (each GPU holds its own copy until the process ends).
+// Host code never passes `scratch` itself to a kernel (on the host it names
+// a stand-in, not the device address): the address is resolved once per
+// device with hipGetSymbolAddress, with that device current, and kept.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[PA_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+pa_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return PA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
+// pa_varlen_fwd, pa_varlen_fwd_fp8, pa_varlen_fwd_ex and
+// pa_varlen_fwd_noalloc: fp8 selects the E4M3 cache with its per-KV-head
+// scales; use_scratch puts the partials in `scratch` instead of `workspace`
 pa_status varlen_fwd(const pa_attn_params* p, const pa_plan_info* plan, const int32_t* worklist,
                      const void* q, const void* kv_cache, const int32_t* cu_seqlens_q,
                      const int32_t* seqused_k, const int32_t* block_table, const float* k_scale,
                      const float* v_scale, bool fp8, const float* s_aux, int32_t num_tokens,
                      void* out, float* lse, void* workspace, size_t workspace_bytes,
-                     hipStream_t stream) {
+                     bool use_scratch, hipStream_t stream) {
   pa_status st = pa::check_params(p);
   if (st != PA_OK) return st;
   if (!plan) return PA_ERR_INVALID_ARGUMENT;
@@ -1391,9 +1416,13 @@ pa_status varlen_fwd(const pa_attn_params* p, const pa_plan_info* plan, const in
       (int64_t)plan->num_small_items + plan->num_tiled_items + plan->num_reduce_items;
   if (plan->worklist_bytes != (size_t)(PA_WORKLIST_HEADER_WORDS + n_items * PA_ITEM_WORDS) * 4)
     return PA_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < plan->workspace_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
-  if (plan->workspace_bytes > 0 && (!workspace || !aligned(workspace, 256)))
-    return PA_ERR_INVALID_ARGUMENT;
+  if (use_scratch) {
+    if (plan->workspace_bytes > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE_TOO_SMALL;
+  } else {
+    if (workspace_bytes < plan->workspace_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
+    if (plan->workspace_bytes > 0 && (!workspace || !aligned(workspace, 256)))
+      return PA_ERR_INVALID_ARGUMENT;
+  }
   if (n_items == 0) return PA_OK;
   if (!worklist || !q || !kv_cache || !cu_seqlens_q || !seqused_k || !block_table || !out)
     return PA_ERR_INVALID_ARGUMENT;
@@ -1405,6 +1434,16 @@ pa_status varlen_fwd(const pa_attn_params* p, const pa_plan_info* plan, const in
     return PA_ERR_INVALID_ARGUMENT;
   if (plan->num_small_items > 0 && p->num_heads / p->num_kv_heads > PA_SMALL_MAX_ROWS)
     return PA_ERR_INVALID_ARGUMENT;
+  // every check has passed: only now the first call on a device resolves
+  // its scratch address (no partial row needs clearing: each one is written
+  // before the reduce of the same call reads it)
+  if (use_scratch) {
+    workspace = nullptr;
+    if (plan->workspace_bytes > 0) {
+      st = scratch_address(&workspace);
+      if (st != PA_OK) return st;
+    }
+  }
   AttnArgs a;
   a.items = nullptr;
   a.q = static_cast<const uint16_t*>(q);
@@ -1458,7 +1497,7 @@ pa_status pa_varlen_fwd(const pa_attn_params* p, const pa_plan_info* plan, const
                         hipStream_t stream) {
   return varlen_fwd(p, plan, worklist, q, kv_cache, cu_seqlens_q, seqused_k, block_table, nullptr,
                     nullptr, false, nullptr, num_tokens, out, lse, workspace, workspace_bytes,
-                    stream);
+                    false, stream);
 }
 
 pa_status pa_varlen_fwd_ex(const pa_attn_params* p, const pa_plan_info* plan,
@@ -1471,7 +1510,20 @@ pa_status pa_varlen_fwd_ex(const pa_attn_params* p, const pa_plan_info* plan,
     return PA_ERR_INVALID_ARGUMENT;
   return varlen_fwd(p, plan, worklist, q, kv_cache, cu_seqlens_q, seqused_k, block_table,
                     opt->k_scale, opt->v_scale, opt->kv_dtype == PA_KV_E4M3, opt->s_aux,
-                    num_tokens, out, lse, workspace, workspace_bytes, stream);
+                    num_tokens, out, lse, workspace, workspace_bytes, false, stream);
+}
+
+pa_status pa_varlen_fwd_noalloc(const pa_attn_params* p, const pa_plan_info* plan,
+                                const int32_t* worklist, const void* q, const void* kv_cache,
+                                const int32_t* cu_seqlens_q, const int32_t* seqused_k,
+                                const int32_t* block_table, const pa_fwd_options* opt,
+                                int32_t num_tokens, void* out, float* lse, hipStream_t stream) {
+  if (opt && opt->kv_dtype != PA_KV_BF16 && opt->kv_dtype != PA_KV_E4M3)
+    return PA_ERR_INVALID_ARGUMENT;
+  const bool fp8 = opt && opt->kv_dtype == PA_KV_E4M3;
+  return varlen_fwd(p, plan, worklist, q, kv_cache, cu_seqlens_q, seqused_k, block_table,
+                    opt ? opt->k_scale : nullptr, opt ? opt->v_scale : nullptr, fp8,
+                    opt ? opt->s_aux : nullptr, num_tokens, out, lse, nullptr, 0, true, stream);
 }
 
 pa_status pa_varlen_fwd_fp8(const pa_attn_params* p, const pa_plan_info* plan,
@@ -1482,7 +1534,7 @@ pa_status pa_varlen_fwd_fp8(const pa_attn_params* p, const pa_plan_info* plan,
                             size_t workspace_bytes, hipStream_t stream) {
   return varlen_fwd(p, plan, worklist, q, kv_cache, cu_seqlens_q, seqused_k, block_table, k_scale,
                     v_scale, true, nullptr, num_tokens, out, lse, workspace, workspace_bytes,
-                    stream);
+                    false, stream);
 }
 
 pa_status pa_merge_attn_states(void* out, float* out_lse, const void* prefix_out,

@@ -39,7 +39,8 @@ PLAN_TARGET_CUS = 256          # compute units the planner schedules for (PA_PLA
 EXPORTED = ["pa_status_str", "pa_version", "pa_supported_head_sizes", "pa_plan_varlen",
             "pa_cascade_split", "pa_reshape_and_cache", "pa_varlen_fwd", "pa_merge_attn_states",
             "pa_reshape_and_cache_fp8", "pa_varlen_fwd_fp8", "pa_cascade_decide",
-            "pa_varlen_fwd_ex"]
+            "pa_varlen_fwd_ex", "pa_varlen_fwd_noalloc"]
+NOALLOC_SCRATCH_BYTES = 32 << 20   # PA_NOALLOC_SCRATCH_BYTES
 
 
 class PaError(RuntimeError):
@@ -127,6 +128,10 @@ def lib() -> ctypes.CDLL:
         L.pa_varlen_fwd_ex.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(PlanInfo), _P,
                                        _P, _P, _P, _P, _P, ctypes.POINTER(FwdOptions),
                                        ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P]
+        L.pa_varlen_fwd_noalloc.restype = ctypes.c_int
+        L.pa_varlen_fwd_noalloc.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(PlanInfo),
+                                            _P, _P, _P, _P, _P, _P, ctypes.POINTER(FwdOptions),
+                                            ctypes.c_int32, _P, _P, _P]
         L.pa_merge_attn_states.restype = ctypes.c_int
         L.pa_merge_attn_states.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int32, _P]
@@ -386,6 +391,32 @@ def pa_varlen_fwd_ex(params: AttnParams, plan: PlanInfo, worklist, q, kv_cache, 
         _dev(out, "out", torch.bfloat16), _dev(lse, "lse", torch.float32),
         _dev(workspace, "workspace"), ws_bytes, _stream(stream))
     _check(st, "pa_varlen_fwd_ex")
+
+
+def pa_varlen_fwd_noalloc(params: AttnParams, plan: PlanInfo, worklist, q, kv_cache, cu_seqlens_q,
+                          seqused_k, block_table, out, lse=None, stream=None, k_scale=None,
+                          v_scale=None, s_aux=None):
+    """pa_varlen_fwd_ex without a workspace: the partials go to the library's
+    own device scratch (PA_NOALLOC_SCRATCH_BYTES per GPU)."""
+    import torch
+    fp8 = k_scale is not None or v_scale is not None
+    check_fwd_args(params, plan, worklist, q, kv_cache, cu_seqlens_q, seqused_k, block_table,
+                   out, lse, fp8=fp8)
+    if fp8 and (k_scale is None or v_scale is None or k_scale.numel() != params.num_kv_heads
+                or v_scale.numel() != params.num_kv_heads):
+        raise ValueError("k_scale and v_scale need one entry per KV head")
+    if s_aux is not None and s_aux.numel() != params.num_heads:
+        raise ValueError("s_aux needs one entry per query head")
+    opt = FwdOptions(PA_KV_E4M3 if fp8 else PA_KV_BF16,
+                     _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
+                     _dev(s_aux, "s_aux", torch.float32))
+    st = lib().pa_varlen_fwd_noalloc(
+        ctypes.byref(params), ctypes.byref(plan), _dev(worklist, "worklist", torch.int32),
+        _dev(q, "q", torch.bfloat16), _dev(kv_cache, "kv_cache", torch.uint8 if fp8 else torch.bfloat16),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(seqused_k, "seqused_k", torch.int32),
+        _dev(block_table, "block_table", torch.int32), ctypes.byref(opt), int(q.shape[0]),
+        _dev(out, "out", torch.bfloat16), _dev(lse, "lse", torch.float32), _stream(stream))
+    _check(st, "pa_varlen_fwd_noalloc")
 
 
 def pa_merge_attn_states(out, out_lse, prefix_out, prefix_lse, suffix_out, suffix_lse,

@@ -202,6 +202,29 @@ def test_merge_validation(L):
     assert f(P(0), None, P(0), P(0), P(0), P(0), 0, 2, 64, None) == ops.PA_OK
 
 
+def test_noalloc_rejects_plans_beyond_its_scratch(L):
+    """pa_varlen_fwd_noalloc refuses a plan whose partials exceed
+    PA_NOALLOC_SCRATCH_BYTES, on the host, before any HIP call (fake
+    pointers are never touched)."""
+    B, Lk = 512, 4096
+    p = ops.make_params(B, 64, 8, 256, 16, B * Lk // 16, Lk // 16, True, 0.0625)
+    cu = np.arange(B + 1, dtype=np.int32)
+    sk = np.full(B, Lk, np.int32)
+    _, info = ops.pa_plan_varlen(p, cu, sk, force_splits=64)
+    assert info.workspace_bytes > ops.NOALLOC_SCRATCH_BYTES
+    P = ctypes.c_void_p
+    st = L.pa_varlen_fwd_noalloc(ctypes.byref(p), ctypes.byref(info), P(0x1000), P(0x2000),
+                                 P(0x3000), P(0x4000), P(0x5000), P(0x6000), None, B, P(0x7000),
+                                 P(0x8000), None)
+    assert st == ops.PA_ERR_WORKSPACE_TOO_SMALL
+    # an invalid cache format is refused as well
+    opt = ops.FwdOptions(7, None, None, None)
+    st = L.pa_varlen_fwd_noalloc(ctypes.byref(p), ctypes.byref(info), P(0x1000), P(0x2000),
+                                 P(0x3000), P(0x4000), P(0x5000), P(0x6000), ctypes.byref(opt), B,
+                                 P(0x7000), P(0x8000), None)
+    assert st == ops.PA_ERR_INVALID_ARGUMENT
+
+
 def test_merge_rejects_lse_aliasing(L):
     """out_lse may not overlap prefix_lse or suffix_lse (rows of 4 tokens x
     2 heads = 8 floats = 32 bytes); out may still alias either output."""
