@@ -125,6 +125,123 @@ int32_t* emit_by_cost(const std::vector<Item>& items, int32_t* dst) {
   return dst;
 }
 
+// Items of one kind as a longest-first queue, and the proportional merge of
+// a small-row and a tiled queue: the kind further behind its share goes
+// next, so that HBM-bound small-row workgroups and matrix-core-bound tiled
+// ones share the compute units throughout the launch.
+void merge_proportional(const std::vector<const Item*>& qs, const std::vector<const Item*>& qt,
+                        std::vector<const Item*>& out) {
+  const uint64_t ns = qs.size(), nt = qt.size();
+  uint64_t is = 0, itd = 0;
+  while (is < ns || itd < nt) {
+    const bool take_tiled = itd < nt && (is >= ns || itd * ns <= is * nt);
+    out.push_back(take_tiled ? qt[itd++] : qs[is++]);
+  }
+}
+
+// The order of a mixed launch.  Workgroup i of a launch runs on XCD i %
+// kXcds (measured on MI355X for every workgroup of a launch), and each XCD
+// has its own L2: the tiled row blocks of one (sequence, KV head) read the
+// same K/V tiles, so they are kept on one XCD (its L2 then fetches those
+// tiles once, not once per XCD).  Groups go to the XCD with the least tiled
+// work so far, largest groups first; small-row items, longest first, fill
+// each XCD's queue up to an equal share of the launch, least-loaded XCD
+// first; each queue is merged in proportion; the queues are interleaved so
+// that position p holds an item of queue p % kXcds (a queue that runs out
+// early lends its slots to the longest one).
+constexpr int kXcds = 8;
+void emit_mixed(const std::vector<Item>& small, const std::vector<Item>& tiled, int32_t num_kv_heads,
+                int32_t* dst) {
+  // thread-local buffers that keep their capacity between calls, bound once
+  // to references (each access to a thread_local of a shared library may
+  // cost a TLS lookup)
+  thread_local std::vector<uint32_t> os_tls, ot_tls;
+  thread_local std::vector<int32_t> gid_tls, gkey_tls, gorder_tls;
+  thread_local std::vector<int64_t> gcost_tls;
+  thread_local std::vector<int8_t> gxcd_tls;
+  thread_local std::vector<const Item*> qt_tls[kXcds], qs_tls[kXcds], q_tls[kXcds];
+  std::vector<uint32_t>& os = os_tls;
+  std::vector<uint32_t>& ot = ot_tls;
+  std::vector<int32_t>& gid_of_key = gid_tls;
+  std::vector<int32_t>& gkey = gkey_tls;
+  std::vector<int32_t>& gorder = gorder_tls;
+  std::vector<int64_t>& gcost = gcost_tls;
+  std::vector<int8_t>& gxcd = gxcd_tls;
+  std::vector<const Item*>* qt = qt_tls;
+  std::vector<const Item*>* qs = qs_tls;
+  std::vector<const Item*>* q = q_tls;
+  order_by_cost(small, os);
+  order_by_cost(tiled, ot);
+  // tiled groups (sequence x KV heads + KV head), numbered in order of first
+  // appearance in the longest-first list
+  int32_t max_seq = 0;
+  for (const Item& it : tiled) max_seq = std::max(max_seq, it.w[0]);
+  gid_of_key.assign((size_t)(max_seq + 1) * num_kv_heads, -1);
+  gkey.clear();
+  gcost.clear();
+  for (uint32_t i : ot) {
+    const int32_t key = tiled[i].w[0] * num_kv_heads + tiled[i].w[1];
+    if (gid_of_key[key] < 0) {
+      gid_of_key[key] = (int32_t)gcost.size();
+      gkey.push_back(key);
+      gcost.push_back(0);
+    }
+    gcost[gid_of_key[key]] += tiled[i].cost;
+  }
+  gorder.resize(gcost.size());
+  for (size_t g = 0; g < gorder.size(); ++g) gorder[g] = (int32_t)g;
+  std::stable_sort(gorder.begin(), gorder.end(),
+                   [&gcost](int32_t a, int32_t b) { return gcost[a] > gcost[b]; });
+  int64_t work[kXcds] = {};
+  gxcd.resize(gcost.size());
+  for (int32_t g : gorder) {
+    int best = 0;
+    for (int x = 1; x < kXcds; ++x)
+      if (work[x] < work[best]) best = x;
+    gxcd[g] = (int8_t)best;
+    work[best] += gcost[g];
+  }
+  for (int x = 0; x < kXcds; ++x) {
+    qt[x].clear();
+    qs[x].clear();
+    q[x].clear();
+  }
+  for (uint32_t i : ot) {
+    const int32_t key = tiled[i].w[0] * num_kv_heads + tiled[i].w[1];
+    qt[gxcd[gid_of_key[key]]].push_back(&tiled[i]);
+  }
+  const size_t total = small.size() + tiled.size();
+  for (uint32_t i : os) {
+    int best = -1;
+    for (int x = 0; x < kXcds; ++x) {
+      const size_t cap = total / kXcds + ((size_t)x < total % kXcds ? 1 : 0);
+      if (qt[x].size() + qs[x].size() >= cap) continue;
+      if (best < 0 || work[x] < work[best]) best = x;
+    }
+    if (best < 0) {   // every queue at its share (tiled groups overfilled some)
+      best = 0;
+      for (int x = 1; x < kXcds; ++x)
+        if (qt[x].size() + qs[x].size() < qt[best].size() + qs[best].size()) best = x;
+    }
+    qs[best].push_back(&small[i]);
+    work[best] += small[i].cost;
+  }
+  for (int x = 0; x < kXcds; ++x) merge_proportional(qs[x], qt[x], q[x]);
+  size_t head[kXcds] = {};
+  for (size_t pos = 0; pos < total; ++pos) {
+    int x = (int)(pos % kXcds);
+    if (head[x] == q[x].size()) {   // lend the slot to the queue with the most left
+      int best = -1;
+      for (int y = 0; y < kXcds; ++y)
+        if (head[y] < q[y].size() && (best < 0 || q[y].size() - head[y] > q[best].size() - head[best]))
+          best = y;
+      x = best;
+    }
+    std::memcpy(dst, q[x][head[x]++]->w, sizeof(Item::w));
+    dst += PA_ITEM_WORDS;
+  }
+}
+
 }  // namespace
 
 pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
@@ -348,24 +465,12 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
   // close in time and their keys warm in L2
   int32_t* dst = wl + PA_WORKLIST_HEADER_WORDS;
   if (!small_items.empty() && !tiled_items.empty()) {
-    // one mixed launch: each kind longest first, the two merged in
-    // proportion to their counts (the kind further behind its share goes
-    // next), so that the HBM-bound small-row items and the matrix-core-bound
-    // tiled items share the compute units throughout the launch (measured
-    // on chunked_prefill_mix: 194 us against 208 us for one merged
-    // longest-first order, 215 us small items first, 232 us tiled first)
-    thread_local std::vector<uint32_t> os, ot;
-    order_by_cost(small_items, os);
-    order_by_cost(tiled_items, ot);
-    const uint64_t ns = os.size(), nt = ot.size();
-    uint64_t is = 0, itd = 0;
-    while (is < ns || itd < nt) {
-      // tiled next when its fraction done is not ahead of the small items'
-      const bool take_tiled = itd < nt && (is >= ns || itd * ns <= is * nt);
-      const Item& it = take_tiled ? tiled_items[ot[itd++]] : small_items[os[is++]];
-      std::memcpy(dst, it.w, sizeof(it.w));
-      dst += PA_ITEM_WORDS;
-    }
+    // one mixed launch: per XCD, each kind longest first, merged in
+    // proportion to their counts (measured on chunked_prefill_mix before the
+    // XCD queues: 194 us against 208 us for one merged longest-first order,
+    // 215 us small items first, 232 us tiled first)
+    emit_mixed(small_items, tiled_items, Hkv, dst);
+    dst += (small_items.size() + tiled_items.size()) * PA_ITEM_WORDS;
   } else {
     dst = emit_by_cost(small_items, dst);
     dst = emit_by_cost(tiled_items, dst);

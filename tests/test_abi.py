@@ -410,22 +410,40 @@ def test_fp8_cache_plan(L):
     assert e.value.status == ops.PA_ERR_INVALID_ARGUMENT
 
 def test_mixed_launch_order(L):
-    """A mixed launch lists each kind longest first, merged in proportion to
-    their counts: after m items the number of tiled items is within one of
-    m * (tiled items / all items)."""
+    """A mixed launch keeps each (sequence, KV head)'s tiled row blocks on one
+    XCD (workgroup i runs on XCD i % 8): every group's items share one
+    position residue mod 8.  Within each residue class each kind is longest
+    first and the two are merged in proportion to their counts (after m items
+    the number of tiled items is within one of m * tiled / all); the XCDs'
+    tiled work differs by less than the largest group."""
     wl = W.make("chunked_prefill_mix", materialise=False)
     p = ops.make_params(wl.B, wl.H, wl.Hkv, wl.D, wl.BS, wl.num_blocks, wl.block_table.shape[1],
                         True, wl.scale)
     words, info = ops.pa_plan_varlen(p, wl.cu_seqlens_q, wl.k_lens)
     items, _ = parse(words, info)
+    pos = np.arange(len(items))
     tiled = items[:, 7] == 1
-    for kind in (False, True):
-        it = items[tiled == kind]
-        cost = (it[:, 5] - it[:, 4]).astype(np.int64) * (it[:, 3] if kind else 128)
-        assert np.all(np.diff(cost) <= 0)
-    n, nt = len(items), int(tiled.sum())
-    m = np.arange(1, n + 1)
-    assert np.all(np.abs(np.cumsum(tiled) - m * nt / n) <= 1.0)
+    groups = {}
+    for i in np.where(tiled)[0]:
+        groups.setdefault((items[i, 0], items[i, 1]), set()).add(i % 8)
+    assert all(len(x) == 1 for x in groups.values())
+    assert len(items) % 8 == 0       # equal queues: no slot is lent
+    gwork = {}
+    cost_all = (items[:, 5] - items[:, 4]).astype(np.int64) * np.where(tiled, items[:, 3], 128)
+    for i in np.where(tiled)[0]:
+        gwork[(items[i, 0], items[i, 1])] = gwork.get((items[i, 0], items[i, 1]), 0) + cost_all[i]
+    xwork = [int(cost_all[(pos % 8 == x) & tiled].sum()) for x in range(8)]
+    assert max(xwork) - min(xwork) <= max(gwork.values())
+    for x in range(8):
+        sub = items[pos % 8 == x]
+        t = sub[:, 7] == 1
+        for kind in (False, True):
+            it = sub[t == kind]
+            cost = (it[:, 5] - it[:, 4]).astype(np.int64) * (it[:, 3] if kind else 128)
+            assert np.all(np.diff(cost) <= 0)
+        n, nt = len(sub), int(t.sum())
+        m = np.arange(1, n + 1)
+        assert np.all(np.abs(np.cumsum(t) - m * nt / n) <= 1.0)
 
 
 def test_large_plan_order_is_stable(L):
