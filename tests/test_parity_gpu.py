@@ -199,9 +199,14 @@ PREFILL_ONLY = [
     (64, 2, 3, 64, False, ((100, 130), (9, 9)), 2),
     (128, 1, 2, 16, True, ((600, 600), (20, 10)), 5),
     (256, 4, 1, 32, True, ((70, 70), (33, 180)), 0),
-    # long enough for 256-row blocks at D = 128 (2048+ query tokens on average)
+    # long enough for 256-row blocks at D = 128 (2048+ query tokens on average):
+    # one token per row at G = 1, eight rows per token at G = 8, rows that see
+    # no key where Lq > Lk, block sizes 16 to 128 and 48
     (128, 4, 2, 32, True, ((2100, 2100), (2050, 2400)), 0),
     (128, 4, 2, 16, False, ((2300, 2300), (1900, 2000)), 3),
+    (128, 1, 3, 64, True, ((2500, 2400), (1700, 1900)), 0),
+    (128, 8, 1, 128, True, ((2049, 4100), (2100, 2100)), 2),
+    (128, 4, 2, 48, True, ((2100, 2100), (2050, 2400)), 0),
 ]
 
 

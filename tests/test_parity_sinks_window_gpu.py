@@ -29,6 +29,7 @@ CASES = [
     (64, 4, 2, 32, ((300, 300), (100, 400)), 64, True, 0, False),
     (128, 4, 2, 32, ((2100, 2100), (2050, 2300)), 700, True, 0, False),
     (128, 4, 2, 16, ((2200, 2200), (2000, 2000)), 1500, True, 2, True),
+    (128, 2, 2, 64, ((2300, 2300), (2100, 2600)), 100, True, 0, False),
 ]
 
 
