@@ -127,7 +127,9 @@ class Step:
                                       ctypes.byref(info))
         if st != 0:
             raise ops.PaError(st, "pa_plan_varlen")
-        self.worklist.copy_(buf, non_blocking=True)
+        # the upload is a kernel of the compute stream (a copy-engine transfer
+        # would make the next kernel wait for the engine's completion signal)
+        ops.pa_upload_words(buf, self.worklist)
         ev = torch.cuda.Event()
         ev.record()
         self.copy_done[k] = ev

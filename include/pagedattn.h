@@ -149,6 +149,23 @@ pa_status pa_plan_varlen(const pa_attn_params* p,
                          pa_plan_info* info);
 
 /* ------------------------------------------------------------------------
+ * pa_upload_words -- copy n_words int32 words (a work list written by
+ * pa_plan_varlen) from pinned host memory to device memory with a kernel on
+ * `stream`.  A copy-engine transfer on the same stream makes the next kernel
+ * wait for the engine's completion signal (25-40 us measured on MI355X with
+ * a 100 KB work list); this copy is an ordinary kernel of the stream, so the
+ * attention launch behind it starts as after any other kernel.
+ *   host_src   pinned host memory mapped for the device (hipHostMalloc,
+ *              torch pin_memory()), 16-byte aligned; the caller keeps it
+ *              unchanged until the copy has run (an event after this call)
+ *   dev_dst    device memory, 16-byte aligned, n_words int32
+ * Errors: PA_ERR_INVALID_ARGUMENT (null pointers, misalignment, n_words < 0,
+ * or host_src not device-mapped pinned memory), PA_ERR_HIP (launch).
+ * ------------------------------------------------------------------------ */
+pa_status pa_upload_words(const int32_t* host_src, int32_t* dev_dst, int64_t n_words,
+                          hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * pa_cascade_split -- host-side metadata of the two cascade passes
  * ("FlashAttention 在 vLLM 中的实现分析", section 6.3): a prefix pass in
  * which all num_tokens queries form ONE pseudo-sequence attending

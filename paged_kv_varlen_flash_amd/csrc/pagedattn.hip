@@ -244,38 +244,84 @@ __device__ __forceinline__ int64_t ld_uniform64(const int64_t* p) {
 }
 
 // ---------------------------------------------------------------------------
-// reshape_and_cache: one wave per token (four tokens per workgroup).  The
-// token's slot is one scalar load; the lanes walk its K row and its V row in
-// 16-byte chunks, two chunks per plane in flight per lane, so no index needs
-// a division.  Slots outside [0, num_slots) are skipped.
+// reshape_and_cache: one wave per RC_TOKENS_PER_WAVE consecutive tokens (four
+// waves per workgroup).  The lanes walk each token's K row and V row in
+// 16-byte chunks, two chunks per plane per token, so no index needs a
+// division.  The source rows do not depend on the slots, so every load of
+// the wave's tokens is issued before the first slot is tested: one memory
+// latency per wave, not two.  Slots outside [0, num_slots) are skipped.  Two
+// tokens per wave halve the workgroup count, so that a batch of a few
+// thousand tokens is one round of resident workgroups with no short second
+// round at the end.
 // ---------------------------------------------------------------------------
+constexpr int RC_TOKENS_PER_WAVE = 2;
+
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const uint16_t* __restrict__ key, const uint16_t* __restrict__ value, int64_t key_stride,
     int64_t value_stride, uint16_t* __restrict__ cache, const int64_t* __restrict__ slot_mapping,
     int32_t num_tokens, int32_t cpr, int64_t row_elems, int64_t plane, int64_t num_slots) {
-  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
-  if (t >= num_tokens) return;
-  const int64_t slot = ld_uniform64(slot_mapping + t);
-  if (slot < 0 || slot >= num_slots) return;
+  constexpr int TPW = RC_TOKENS_PER_WAVE;
+  const int t0 = __builtin_amdgcn_readfirstlane((blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW);
+  if (t0 >= num_tokens) return;
   const int lane = threadIdx.x & 63;
-  const uint4* ks = reinterpret_cast<const uint4*>(key + (int64_t)t * key_stride);
-  const uint4* vs = reinterpret_cast<const uint4*>(value + (int64_t)t * value_stride);
-  uint4* kd = reinterpret_cast<uint4*>(cache + slot * row_elems);
-  uint4* vd = reinterpret_cast<uint4*>(cache + plane + slot * row_elems);
+  const int row_bytes = (int)(row_elems * 2);
   for (int c = lane; c < cpr; c += 128) {
-    const bool two = c + 64 < cpr;
-    const uint4 k0 = ks[c], v0 = vs[c];
-    uint4 k1 = k0, v1 = v0;
-    if (two) {
-      k1 = ks[c + 64];
-      v1 = vs[c + 64];
+    // chunk c and chunk c + 64 of each row; a lane without a second chunk
+    // moves its first one twice
+    const int c1 = c + 64 < cpr ? c + 64 : c;
+    u32x4_t k[TPW][2], v[TPW][2];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = min(t0 + i, num_tokens - 1);     // a past-the-end token re-reads the last
+      const u32x4_t* ks = reinterpret_cast<const u32x4_t*>(key + (int64_t)t * key_stride);
+      const u32x4_t* vs = reinterpret_cast<const u32x4_t*>(value + (int64_t)t * value_stride);
+      k[i][0] = __builtin_nontemporal_load(ks + c);
+      v[i][0] = __builtin_nontemporal_load(vs + c);
+      k[i][1] = __builtin_nontemporal_load(ks + c1);
+      v[i][1] = __builtin_nontemporal_load(vs + c1);
     }
-    kd[c] = k0;
-    vd[c] = v0;
-    if (two) {
-      kd[c + 64] = k1;
-      vd[c + 64] = v1;
+    // each token's destination rows as buffer resources, set up once the rows
+    // are requested (the slot loads overlap them; the empty asm keeps the
+    // compiler from hoisting them above the row loads): a token past the end
+    // or with a skipped slot gets 0 records, so its stores are dropped and
+    // the loop holds no branch (the compiler would otherwise sink the loads
+    // into it)
+    const int64_t* sm = slot_mapping;
+    asm volatile("" : "+s"(sm));
+    __amdgpu_buffer_rsrc_t kr[TPW], vr[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int64_t slot = ld_uniform64(sm + min(t0 + i, num_tokens - 1));
+      const bool ok = (t0 + i < num_tokens) & (slot >= 0) & (slot < num_slots);
+      const int64_t off = (slot * row_elems) & -(int64_t)ok;
+      kr[i] = __builtin_amdgcn_make_buffer_rsrc(cache + off, 0, row_bytes & -(int)ok, 0x00020000);
+      vr[i] = __builtin_amdgcn_make_buffer_rsrc(cache + plane + off, 0, row_bytes & -(int)ok,
+                                                0x00020000);
     }
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      __builtin_amdgcn_raw_buffer_store_b128(k[i][0], kr[i], 16 * c, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(v[i][0], vr[i], 16 * c, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(k[i][1], kr[i], 16 * c1, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(v[i][1], vr[i], 16 * c1, 0, 0);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Work-list upload: thread i copies words [4i, 4i + 4) (the last thread the
+// remainder) from pinned host memory, read over the bus by the kernel itself.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void upload_words_kernel(const int32_t* __restrict__ src,
+                                                           int32_t* __restrict__ dst,
+                                                           int64_t n_words) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t w = 4 * i;
+  if (w + 4 <= n_words) {
+    reinterpret_cast<u32x4_t*>(dst)[i] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4_t*>(src) + i);
+  } else {
+    for (int64_t k = w; k < n_words; ++k) dst[k] = src[k];
   }
 }
 
@@ -1303,6 +1349,27 @@ pa_status launch_fwd(const AttnArgs& base, const pa_plan_info* plan, const int32
 
 extern "C" {
 
+pa_status pa_upload_words(const int32_t* host_src, int32_t* dev_dst, int64_t n_words,
+                          hipStream_t stream) {
+  if (n_words < 0 || n_words > ((int64_t)1 << 34)) return PA_ERR_INVALID_ARGUMENT;
+  if (n_words == 0) return PA_OK;
+  if (!host_src || !dev_dst || !aligned(host_src, 16) || !aligned(dev_dst, 16))
+    return PA_ERR_INVALID_ARGUMENT;
+  // the device's address of the pinned buffer; fails for memory the device
+  // cannot read, which is then an error instead of a fault
+  void* src_dev = nullptr;
+  if (hipHostGetDevicePointer(&src_dev, const_cast<int32_t*>(host_src), 0) != hipSuccess ||
+      !src_dev) {
+    (void)hipGetLastError();
+    return PA_ERR_INVALID_ARGUMENT;
+  }
+  const int64_t n16 = (n_words + 3) / 4;
+  const uint32_t blocks = (uint32_t)((n16 + 255) / 256);
+  hipLaunchKernelGGL(upload_words_kernel, dim3(blocks), dim3(256), 0, stream,
+                     static_cast<const int32_t*>(src_dev), dev_dst, n_words);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 pa_status pa_reshape_and_cache(const void* key, const void* value, int64_t key_row_stride,
                                int64_t value_row_stride, void* kv_cache,
                                const int64_t* slot_mapping, int32_t num_tokens,
@@ -1321,7 +1388,8 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, int64_t key_r
     return PA_ERR_INVALID_ARGUMENT;
   const int64_t plane = (int64_t)num_blocks * block_size * row;
   const int32_t cpr = (int32_t)(row / 8);
-  const uint32_t blocks = (uint32_t)((num_tokens + 3) / 4);
+  const int32_t per_block = 4 * RC_TOKENS_PER_WAVE;
+  const uint32_t blocks = (uint32_t)((num_tokens + per_block - 1) / per_block);
   hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(blocks), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),
                      key_row_stride, value_row_stride, static_cast<uint16_t*>(kv_cache),

@@ -39,7 +39,7 @@ PLAN_TARGET_CUS = 256          # compute units the planner schedules for (PA_PLA
 EXPORTED = ["pa_status_str", "pa_version", "pa_supported_head_sizes", "pa_plan_varlen",
             "pa_cascade_split", "pa_reshape_and_cache", "pa_varlen_fwd", "pa_merge_attn_states",
             "pa_reshape_and_cache_fp8", "pa_varlen_fwd_fp8", "pa_cascade_decide",
-            "pa_varlen_fwd_ex", "pa_varlen_fwd_noalloc"]
+            "pa_varlen_fwd_ex", "pa_varlen_fwd_noalloc", "pa_upload_words"]
 NOALLOC_SCRATCH_BYTES = 32 << 20   # PA_NOALLOC_SCRATCH_BYTES
 
 
@@ -132,6 +132,8 @@ def lib() -> ctypes.CDLL:
         L.pa_varlen_fwd_noalloc.argtypes = [ctypes.POINTER(AttnParams), ctypes.POINTER(PlanInfo),
                                             _P, _P, _P, _P, _P, _P, ctypes.POINTER(FwdOptions),
                                             ctypes.c_int32, _P, _P, _P]
+        L.pa_upload_words.restype = ctypes.c_int
+        L.pa_upload_words.argtypes = [_P, _P, ctypes.c_int64, _P]
         L.pa_merge_attn_states.restype = ctypes.c_int
         L.pa_merge_attn_states.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int32, _P]
@@ -245,6 +247,24 @@ def _dev(t, what, dtype=None):
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def pa_upload_words(host_words, device_words, stream=None):
+    """Copy a pinned host int32 tensor into a device int32 tensor of the same
+    size with a kernel on the stream (pa_upload_words).  The host tensor must
+    stay unchanged until the copy has run."""
+    import torch
+    if not isinstance(host_words, torch.Tensor) or host_words.is_cuda or \
+            not host_words.is_pinned():
+        raise TypeError("host_words must be a pinned host tensor")
+    if host_words.dtype != torch.int32 or not host_words.is_contiguous():
+        raise TypeError("host_words must be contiguous int32")
+    if device_words.numel() != host_words.numel() or not device_words.is_contiguous():
+        raise ValueError("device_words must be a contiguous tensor of the same size")
+    st = lib().pa_upload_words(ctypes.c_void_p(host_words.data_ptr()),
+                               _dev(device_words, "device_words", torch.int32),
+                               host_words.numel(), _stream(stream))
+    _check(st, "pa_upload_words")
 
 
 def pa_reshape_and_cache(key, value, kv_cache, slot_mapping, stream=None):

@@ -695,3 +695,15 @@ def test_window_params_validation(L):
     assert L.pa_varlen_fwd_ex(ctypes.byref(p), ctypes.byref(info), P(0x1000), P(0x2000), P(0x3000),
                               P(0x4000), P(0x5000), P(0x6000), ctypes.byref(bad), info.num_tokens,
                               P(0x7000), P(0x8000), P(0x10000), 1 << 30, None) == E
+
+
+def test_upload_words_rejects_bad_arguments_before_any_launch(L):
+    P = ctypes.c_void_p
+    buf = (ctypes.c_int32 * 8)()
+    a = ctypes.addressof(buf)
+    a16 = a + (-a) % 16 if (a % 16) else a
+    bad = [(P(a16), P(a16), -1), (None, P(a16), 4), (P(a16), None, 4),
+           (P(a16 + 4), P(a16), 4), (P(a16), P(a16 + 4), 4)]
+    for src, dst, n in bad:
+        assert L.pa_upload_words(src, dst, n, None) == 1     # PA_ERR_INVALID_ARGUMENT
+    assert L.pa_upload_words(None, None, 0, None) == 0       # nothing to copy

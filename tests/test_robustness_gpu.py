@@ -10,7 +10,11 @@ fp64 oracle:
   oracle's single pass;
 * the calls captured into a HIP graph and replayed (the ahead-of-time
   schedule of section 7 exists so that they can be): every replay, with the
-  program's own eager work between replays, matches the oracle."""
+  program's own eager work between replays, matches the oracle;
+* the work-list upload kernel copies exactly, and refuses host memory the
+  device cannot read."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -248,3 +252,27 @@ def test_graph_capture_cascade():
                 label=label)
 
     _replays(g, check, reset)
+
+
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 1023, 70001])
+def test_upload_words_copies_exactly(n):
+    """pa_upload_words: the device copy of a pinned host buffer equals it word
+    for word, for sizes that end inside a 16-byte chunk too."""
+    say(f"upload words n={n}")
+    rng = np.random.default_rng(9000 + n)
+    host = torch.from_numpy(rng.integers(-2**31, 2**31 - 1, size=n, dtype=np.int32)).pin_memory()
+    dev = torch.full((n,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    ops.pa_upload_words(host, dev)
+    torch.cuda.synchronize()
+    assert torch.equal(dev.cpu(), host)
+
+
+def test_upload_words_rejects_unpinned_host_memory():
+    """A host buffer the device cannot read is an error, not a launch."""
+    host = np.arange(64, dtype=np.int32)
+    dev = torch.zeros(64, dtype=torch.int32, device="cuda")
+    st = ops.lib().pa_upload_words(host.ctypes.data_as(ctypes.c_void_p),
+                                   ctypes.c_void_p(dev.data_ptr()), 64, None)
+    torch.cuda.synchronize()
+    assert st == 1
+    assert int(dev.abs().sum()) == 0
