@@ -298,13 +298,24 @@ def measure(name, args, dev, flush, cpu_unit=None, fp8=False, single_pass=False,
     per_step = time_steps(step, args.steps, args.warmup)
     t_mean, t_med = time_attention(step, args.kernel_reps, flush)
     kv = wl.kv_read_bytes() // (2 if fp8 else 1)
+    single_pass_kv = None
+    if step.cascade is not None:
+        # the cascade reads the shared prefix once (prefix pass) and each
+        # sequence's own suffix (suffix pass): those are its algorithmic bytes;
+        # the single-pass bytes (every sequence reading the prefix) are context
+        P = wl.spec.shared_prefix
+        single_pass_kv = kv
+        kv = int(2 * (P + (wl.k_lens.astype(np.int64) - P).sum()) * wl.Hkv * wl.D * 2)
     if window:
         # keys inside the window only (decode rows: the last W keys)
         kv = int(2 * np.minimum(wl.k_lens.astype(np.int64), window).sum() * wl.Hkv * wl.D
                  * (1 if fp8 else 2))
     flops = wl.attention_flops()
     res = {"workload": name, "wl": wl, "ms_per_step": per_step * 1e3, "attn_mean_s": t_mean,
-           "attn_median_s": t_med, "kv_bytes": kv, "flops": flops, "plan": step.info.as_dict()}
+           "attn_median_s": t_med, "kv_bytes": kv, "flops": flops, "plan": step.info.as_dict(),
+           "single_pass_kv_bytes": single_pass_kv,
+           "cascade_plans": None if step.cascade is None else
+           (step.cascade.prefix.info.as_dict(), step.cascade.suffix.info.as_dict())}
     if cpu_unit:
         print(f"bench: oracle CPU baseline on {name}", file=sys.stderr, flush=True)
         res["cpu"] = cpu_baseline(wl, args.cpu_seconds, step if fp8 else None, cpu_unit)
@@ -314,7 +325,13 @@ def measure(name, args, dev, flush, cpu_unit=None, fp8=False, single_pass=False,
 
 
 def kernel_names(res, fp8):
-    """The kernels of one attention call, from its plan."""
+    """The kernels of one attention call, from its plan (a cascade: both
+    passes' kernels and the merge)."""
+    if res.get("cascade_plans"):
+        pre, suf = res["cascade_plans"]
+        return ("prefix pass: " + kernel_names(dict(res, plan=pre, cascade_plans=None), fp8) +
+                "; suffix pass: " + kernel_names(dict(res, plan=suf, cascade_plans=None), fp8) +
+                "; merge_states_kernel")
     p, D = res["plan"], res["wl"].D
     tag = f"<{D}{', fp8' if fp8 else ''}>"
     if p["num_small_items"] and p["num_tiled_items"]:
@@ -341,7 +358,11 @@ def hbm_roofline(res, fp8, traffic_key):
             "kernel": "pa_varlen_fwd%s: %s" % ("_fp8" if fp8 else "", kernel_names(res, fp8)),
             "per_launch_bytes": res["kv_bytes"],
             "avg_launch_us": round(res["attn_mean_s"] * 1e6, 2),
-            "median_launch_us": round(res["attn_median_s"] * 1e6, 2)}
+            "median_launch_us": round(res["attn_median_s"] * 1e6, 2),
+            **({"single_pass_bytes": res["single_pass_kv_bytes"],
+                "single_pass_equivalent_GBps": round(res["single_pass_kv_bytes"] /
+                                                     res["attn_mean_s"] / 1e9, 1)}
+               if res.get("single_pass_kv_bytes") else {})}
 
 
 def mfma_roofline(res, fp8, traffic_key):
