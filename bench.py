@@ -429,7 +429,7 @@ METRIC = "decode KV-read GB/s + prefill TFLOP/s, as % of MI355X roofline"
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path "
               f"(--gpus {args.gpus} requested); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch

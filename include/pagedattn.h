@@ -37,7 +37,7 @@ extern "C" {
 typedef enum {
   PA_OK = 0,
   PA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, inconsistent lengths */
-  PA_ERR_UNSUPPORTED = 2,        /* a valid configuration this build does not instantiate */
+  PA_ERR_UNSUPPORTED = 2,        /* a valid configuration the library does not instantiate */
   PA_ERR_WORKSPACE_TOO_SMALL = 3,/* worklist or workspace smaller than the plan needs */
   PA_ERR_HIP = 4                 /* a kernel launch failed (hipGetLastError) */
 } pa_status;
