@@ -707,3 +707,14 @@ def test_upload_words_rejects_bad_arguments_before_any_launch(L):
     for src, dst, n in bad:
         assert L.pa_upload_words(src, dst, n, None) == 1     # PA_ERR_INVALID_ARGUMENT
     assert L.pa_upload_words(None, None, 0, None) == 0       # nothing to copy
+
+
+def test_plan_with_no_query_tokens(L):
+    """A batch whose sequences have no query tokens plans no work: the forward
+    call then launches nothing and writes nothing."""
+    p = params(batch=3, max_blocks_per_seq=4)
+    words, info = ops.pa_plan_varlen(p, np.array([0, 0, 0, 0], np.int32),
+                                     np.array([0, 30, 1], np.int32))
+    assert info.num_tokens == 0
+    assert info.num_small_items == info.num_tiled_items == info.num_reduce_items == 0
+    assert info.workspace_bytes == 0 or info.num_partial_rows == 0

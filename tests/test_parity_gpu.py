@@ -224,6 +224,33 @@ def test_prefill_only(case):
     assert plan.info.tiled_rows == (256 if wide else 128)
 
 
+# Degenerate batches: sequences with no query tokens (anywhere in the
+# batch, or every one: nothing to compute, nothing written), sequences with
+# no keys (rows with no visible key: out 0, lse -inf), one-key decodes, a
+# 256-token block size, and a batch of 1024 short decodes.
+DEGENERATE = [
+    # D, G, Hkv, BS, causal, (Lq, Lk) per sequence
+    (128, 4, 2, 32, True, ((0, 100), (1, 50), (0, 0), (5, 5), (40, 300), (0, 7))),
+    (64, 4, 2, 16, True, ((0, 0), (0, 30), (0, 1))),
+    (128, 4, 2, 16, False, ((1, 0), (3, 0), (20, 0))),
+    (128, 8, 1, 16, True, ((1, 0), (1, 1), (1, 1), (2, 1))),
+    (128, 4, 2, 256, True, ((1, 700), (300, 900), (1, 256), (257, 257))),
+    (128, 4, 2, 16, True, tuple((1, 64) for _ in range(1024))),
+]
+
+
+@pytest.mark.parametrize("case", range(len(DEGENERATE)))
+def test_degenerate_batches(case):
+    D, G, Hkv, BS, causal, seqs = DEGENERATE[case]
+    spec = W.Spec(name=f"degenerate{case}", num_heads=G * Hkv, num_kv_heads=Hkv, head_size=D,
+                  block_size=BS, causal=causal, seed=7600 + case, fixed=seqs, min_num_blocks=3)
+    say(f"degenerate case={case} D={D} G={G} Hkv={Hkv} BS={BS} causal={causal} "
+        f"seqs={seqs[:6]}{'...' if len(seqs) > 6 else ''} ({len(seqs)} sequences)")
+    plan = _check_case(spec, np.random.default_rng(7600 + case), 0, f"degenerate{case}")
+    if sum(q for q, _ in seqs) == 0:
+        assert plan.info.num_small_items + plan.info.num_tiled_items == 0
+
+
 def _check_case(spec, rng, force, label, qmul=1.0, smul=1.0):
     q_lens = np.array([a for a, _ in spec.fixed], np.int32)
     k_lens = np.array([b for _, b in spec.fixed], np.int32)
