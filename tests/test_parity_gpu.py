@@ -62,7 +62,8 @@ def test_reshape_and_cache_strided_and_skipped():
 
 # ------------------------------------------------------------ attention
 @pytest.mark.parametrize("name", ["tiny_mixed", "decode_llama8b", "chunked_prefill_mix",
-                                  "chunked_prefill_mix_prefill", "cascade_prefix"])
+                                  "chunked_prefill_mix_prefill", "cascade_prefix",
+                                  "prefill_causal_8k"])
 def test_varlen_fwd_workload(name):
     say(f"varlen_fwd {name}")
     wl = W.make(name)
