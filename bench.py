@@ -339,7 +339,11 @@ def kernel_names(res, fp8):
     elif p["num_small_items"]:
         k = ["attn_small_kernel" + tag]
     elif p["tiled_rows"] == 256:
-        k = ["attn_tiled_wide_kernel" + tag]
+        BS = res["wl"].BS
+        if D == 128 and not fp8 and BS & (BS - 1) == 0:
+            k = ["attn_tiled_dma_kernel<128>"]
+        else:
+            k = ["attn_tiled_wide_kernel" + tag]
     else:
         k = ["attn_tiled_kernel" + tag]
     if p["num_reduce_items"]:

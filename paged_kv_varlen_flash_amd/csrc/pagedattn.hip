@@ -11,6 +11,9 @@
 //                              bound by the matrix cores
 //   attn_tiled_wide_kernel<D>  the same for 256-row blocks: 8 waves share
 //                              each K/V tile (long prefills, D <= 128)
+//   attn_tiled_dma_kernel<128> 256-row blocks of a bf16 cache with a
+//                              power-of-two block size: K/V tiles go from
+//                              HBM to LDS by DMA, two tiles ahead
 //   attn_mixed_kernel<D>       small-row and 128-row items in one launch
 //   split_reduce_kernel<D>     LSE merge of split-KV partials (section 1.3
 //                              num_splits)
@@ -1158,6 +1161,298 @@ __global__ __launch_bounds__(512, 2) void attn_tiled_wide_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// 256-row tiled attention with LDS-DMA tile loads (bf16 cache, D = 128,
+// block size a power of two >= 16): 8 waves of 32 rows share each 64-key
+// K/V tile, one workgroup per compute unit.  Tiles go from HBM straight to
+// LDS (buffer_load_dwordx4 ... lds), two tiles ahead, into a ring of three
+// slots per plane (96 KB): no register holds a tile in flight and no LDS
+// store runs, so a wave's work per tile is its QK^T, softmax and PV alone.
+//   * Each wave issues 2 loads per plane and tile: instruction i (0..15)
+//     fills LDS bytes 1024 i .. 1024 i + 1023 with 8 key rows x 8 chunks of
+//     16 bytes (8 whole 128-byte lines of the cache).  Lane l writes the 16
+//     bytes at 16 l; which chunk a lane fetches sets the layout, chosen so
+//     that the operand reads hit all 64 banks once and their addresses are
+//     one register plus constants.
+//   * A 16-key group lies in one cache block (tiles start on a multiple of
+//     16 keys), so one buffer resource per group covers it; keys past the
+//     range and entries outside [0, NB) read as zeros.
+//   * Block-table entries are vector loads one tile before their tile's
+//     loads, so their waits count in order with the tiles' loads.
+//   * Each slot is an array of its own, named statically by a loop unrolled
+//     by three: the compiler makes an LDS read wait only for LDS-DMA loads
+//     into the array it reads.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+// s_waitcnt with only the vector-memory count bounded (gfx9 encoding)
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <int D>
+__global__ __launch_bounds__(512, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_tiled_dma_kernel(AttnArgs a) {
+  static_assert(D == 128, "LDS-DMA tiled kernel");
+  constexpr int NKT = D / 16, NDT = D / 32, TILE = 64 * 2 * D;
+  __shared__ __attribute__((aligned(1024))) uint8_t ks0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks2[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs2[TILE];
+  auto kslot = [&](auto pc) -> uint8_t* {
+    constexpr int s = decltype(pc)::value % 3;
+    if constexpr (s == 0) return ks0;
+    else if constexpr (s == 1) return ks1;
+    else return ks2;
+  };
+  auto vslot = [&](auto pc) -> uint8_t* {
+    constexpr int s = decltype(pc)::value % 3;
+    if constexpr (s == 0) return vs0;
+    else if constexpr (s == 1) return vs1;
+    else return vs2;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, h = lane >> 5;
+  const Item it = load_item(a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS);
+  const int t0 = it.t0, G = a.G, nrows = it.nrows, kv0 = it.kv0;
+  const int kv1 = min(it.kv1, a.MB * a.BS);
+  const int nt = kv1 > kv0 ? (kv1 - kv0 + 63) >> 6 : 0;
+  const float sl2 = a.scale_log2;
+
+  const int rl = wave * 32 + n;
+  const int r = it.row0 + rl;
+  const bool row_ok = rl < nrows;
+  const int tok = r / G;
+  const int head = it.kvh * G + (r - tok * G);
+  const int row_limit = a.causal ? tok + it.koff : INT_MAX;
+  const int row_lo = a.window > 0 ? tok + it.koff - (a.window - 1) : INT_MIN;
+  const int wave_limit = a.causal ? (it.row0 + wave * 32) / G + it.koff : INT_MAX;
+  const int wave_lo = a.window > 0 ? (it.row0 + wave * 32 + 31) / G + it.koff - (a.window - 1) : INT_MIN;
+  const bool wave_rows = wave * 32 < nrows;
+  const int wave_last = a.causal ? (it.row0 + min(wave * 32 + 31, nrows - 1)) / G + it.koff : INT_MAX;
+
+  bf16x8_t qf[NKT];
+  if (row_ok) {
+    const uint16_t* qp = a.q + ((int64_t)(t0 + tok) * a.H + head) * D + 8 * h;
+#pragma unroll
+    for (int t = 0; t < NKT; ++t) qf[t] = ld16(qp + 16 * t);
+  } else {
+#pragma unroll
+    for (int t = 0; t < NKT; ++t) qf[t] = zero8();
+  }
+
+  // ---- loader.  Instruction i (0..15) of a plane fills LDS bytes
+  // 1024 i .. 1024 i + 1023 with the 8 key rows 8 rg .. 8 rg + 7 (rg = i / 2)
+  // and the 8 chunks 8 ch .. 8 ch + 7 (ch = i % 2) of each: 8 full 128-byte
+  // lines.  Lane l writes 16 bytes at 16 l; which chunk it fetches sets the
+  // layout:
+  //   K: unit 8 p + r8 holds row r8, chunk 8 ch + (p ^ (rg & 1))   (chunk-major)
+  //   V: unit 8 r8 + p holds row r8, chunk 8 ch + (p ^ 4 ((r8 >> 1) & 1))
+  // Wave w issues i = w and i = w + 8: 16-key groups w / 4 and w / 4 + 2, and
+  // the same row within the group (8 ((w / 2) & 1) + r8) and chunk for both.
+  const int64_t row_elems = (int64_t)a.Hkv * D;
+  const int row_bytes = (int)(row_elems * 2);
+  const int rgo = (wave >> 1) & 1, chh = wave & 1;
+  const int voff_k = (8 * rgo + (lane & 7)) * row_bytes + ((8 * chh + ((lane >> 3) ^ rgo)) << 4);
+  const int vr8 = lane >> 3;
+  const int voff_v = (8 * rgo + vr8) * row_bytes + ((8 * chh + ((lane & 7) ^ (4 * ((vr8 >> 1) & 1)))) << 4);
+  const uint8_t* cache_b = reinterpret_cast<const uint8_t*>(a.cache) + (int64_t)it.kvh * D * 2;
+  const int32_t* btrow = a.block_table + (int64_t)it.seq * a.bt_stride;
+  const int bs_log2 = a.bs_log2;
+  const int last_blk = kv1 > 0 ? (kv1 - 1) >> bs_log2 : 0;
+  const int64_t blk_bytes = (int64_t)row_bytes << bs_log2;
+  const int64_t plane_bytes = a.plane * 2;
+  const int grp0 = wave >> 2;              // the wave's two groups: grp0 and grp0 + 2
+  // block-table entries of tile t: lanes 0..3 load group l's, the others a copy
+  auto fetch = [&](int t) -> int {
+    return btrow[min((kv0 + 64 * t + 16 * (lane & 3)) >> bs_log2, last_blk)];
+  };
+  auto load_tile = [&](int t, uint8_t* kd, uint8_t* vd, int ent) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int grp = grp0 + 2 * q;
+      const int g = wave + 8 * q;
+      const int phys = __builtin_amdgcn_readlane(ent, grp);
+      const int key0 = kv0 + 64 * t + 16 * grp;
+      const bool ok = (key0 < kv1) & ((unsigned)phys < (unsigned)a.NB);
+      const int64_t x = (int64_t)phys * blk_bytes + (int64_t)(key0 & (a.BS - 1)) * row_bytes;
+      const int64_t boff = x & -(int64_t)ok;
+      const int nrec = ((min(16, kv1 - key0) - 1) * row_bytes + D * 2) & -(int)ok;
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(cache_b + boff), 0, nrec, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(cache_b + plane_bytes + boff), 0, nrec, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_ptr)(kd + 1024 * g), 16, voff_k, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_ptr)(vd + 1024 * g), 16, voff_v, 0, 0, 0);
+    }
+  };
+  constexpr int kLoadsPerTile = 4;
+
+  // ---- read addresses.  K operand of k-step t, key half u (row r = n + 32u,
+  // chunk C = 2t + h): 2048 (r / 8) + 1024 (C / 8) + 128 ((C % 8) ^ ((r / 8) & 1))
+  // + 16 (r % 8) = kbase + 8192 u + 1024 (t / 4) + 256 (t % 4).  V operand of d
+  // tile dt, 16-key step ks, second half e (row 16 ks + 8 e + r8, local chunk
+  // cl of the tile's 4): vbase(dt % 2) + 4096 ks + 2048 e + 1024 (dt / 2).
+  // Both are conflict-free: the 16 lanes of a K read and the 32 lanes of a
+  // transposing read cover all 64 banks once.
+  const int n8 = n >> 3;
+  const int kbase = 2048 * n8 + 128 * (h ^ (n8 & 1)) + 16 * (n & 7);
+  const int q16 = lane >> 4, s16 = lane & 15;
+  const int r8v = 4 * h + (s16 >> 2);
+  const int clv = 2 * (q16 & 1) + ((s16 & 3) >> 1);
+  const int vbase0 = 128 * r8v + 16 * clv + 8 * (s16 & 1) + 64 * ((r8v >> 1) & 1);
+  const int vbase1 = vbase0 ^ 64;
+
+  float m_run = kNegInf, l_run = 0.f, lr_run = 0.f;
+  f32x16_t o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+
+  // (forced inline: three unrolled calls exceed the inliner's budget, and an
+  // outlined tile would keep O and the row state in scratch memory)
+  auto tile = [&](int j0, const uint8_t* kb, const uint8_t* vb, bool masked) __attribute__((always_inline)) {
+    f32x16_t s[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[u][i] = 0.f;
+#pragma unroll
+    for (int t = 0; t < NKT; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kb + kbase + 8192 * u + 1024 * (t >> 2) + 256 * (t & 3));
+        s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[t], s[u], 0, 0, 0);
+      }
+    float x[32];
+    const int lim = min(kv1 - 1, row_limit) - j0 - 4 * h;
+    const int lim_lo = (row_lo == INT_MIN) ? INT_MIN : row_lo - j0 - 4 * h;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[16 * u + i] = s[u][i];
+    if (masked) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int off = 32 * (i >> 4) + 8 * ((i & 15) >> 2) + (i & 3);
+        x[i] = (off > lim || off < lim_lo) ? kNegInf : x[i];
+      }
+    }
+    float mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, x[i]);
+    mx = max_xor<32>(mx) * sl2;
+    if (__builtin_expect(__any(mx > m_run + kRescaleSlack), 0)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+      lr_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], sl2, neg_m));
+      ps[i & 3] += x[i];
+    }
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    bf16x8_t pb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      pb[ks] = pack_bf16x8(x + 8 * ks);
+      lr_run = add_bf16x8(pb[ks], lr_run);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const uint8_t* p0 = vb + ((dt & 1) ? vbase1 : vbase0) + 4096 * ks + 1024 * (dt >> 1);
+        const bf16x8_t av = cat(lds_read_tr(reinterpret_cast<const uint16_t*>(p0)),
+                                lds_read_tr(reinterpret_cast<const uint16_t*>(p0 + 2048)));
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks], o[dt], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- the loop starts two tiles early (j = -2, -1 only issue loads), so
+  // that no load is in flight on entry: every load is then issued by the
+  // same unrolled code, which keeps the compiler's own wait counts exact.
+  // The lookup of tile 0 and the Q loads land before the loop.
+  int e_cur = nt > 0 ? fetch(0) : 0, e_next;   // entries of tile j+2 at the top of iteration j
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  auto iteration = [&](auto pc, int j) {
+    constexpr int P = decltype(pc)::value;    // slot of tile j (j mod 3)
+    // tile j and tile j+2's entries have landed (only tile j+1's loads may
+    // be in flight); after the barrier every wave is done with tile j-1,
+    // whose slots tile j+2's loads overwrite
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoadsPerTile));
+    // a workgroup barrier with no memory fence: a fence would wait for every
+    // LDS-DMA load in flight, tile j+1's too ("memory" keeps the compiler
+    // from moving LDS accesses across it)
+    asm volatile("s_barrier" ::: "memory");
+    e_next = fetch(j + 3);
+    // the lookup goes out before the tile's loads, so that waiting for it
+    // never waits for them
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile(j + 2, kslot(IntC<P + 2>{}), vslot(IntC<P + 2>{}), e_cur);
+    e_cur = e_next;
+    const int j0 = kv0 + 64 * j;
+    if (j >= 0 && wave_rows && j0 <= wave_last)
+      tile(j0, kslot(pc), vslot(pc), j0 + 64 > kv1 || j0 + 63 > wave_limit || j0 < wave_lo);
+  };
+  for (int j = nt > 0 ? -2 : 0;;) {
+    if (j >= nt) break;
+    iteration(IntC<1>{}, j++);
+    if (j >= nt) break;
+    iteration(IntC<2>{}, j++);
+    if (j >= nt) break;
+    iteration(IntC<0>{}, j++);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+
+  // ---- epilogue (as attn_tiled_kernel)
+  const float l = sum_xor<32>(l_run);
+  float lr = sum_xor<32>(lr_run);
+  if (!row_ok) return;
+  float mr = m_run, ll = l, fo = 1.f;
+  if (a.s_aux && it.prow < 0) fo = add_sink(a.s_aux[head] * kLog2e, mr, ll, lr);
+  const bool empty = !(ll > 0.f);
+  const float inv = empty ? 0.f : fo / lr;
+  const float lse_v = empty ? kNegInf : (mr + __log2f(ll)) * kLn2;
+  if (it.prow < 0) {
+    const int64_t orow = (int64_t)(t0 + tok) * a.H + head;
+    uint16_t* op = a.out + orow * D + 4 * h;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) {
+        uint2 w;
+        w.x = pack_bf16x2(o[dt][4 * ig] * inv, o[dt][4 * ig + 1] * inv);
+        w.y = pack_bf16x2(o[dt][4 * ig + 2] * inv, o[dt][4 * ig + 3] * inv);
+        *reinterpret_cast<uint2*>(op + 32 * dt + 8 * ig) = w;
+      }
+    if (h == 0 && a.lse) a.lse[orow] = lse_v;
+  } else {
+    float* pp = a.part_o + (int64_t)(it.prow + rl) * D + 4 * h;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig)
+        *reinterpret_cast<f32x4_t*>(pp + 32 * dt + 8 * ig) =
+            f32x4_t{o[dt][4 * ig] * inv, o[dt][4 * ig + 1] * inv, o[dt][4 * ig + 2] * inv,
+                    o[dt][4 * ig + 3] * inv};
+    if (h == 0) a.part_lse[it.prow + rl] = lse_v;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Mixed launch: when a batch has both decode-like and prefill rows, one grid
 // runs both kinds of item (word 7 of an item: 0 small-row, 1 tiled), in the
 // planner's longest-first order, so the HBM-bound small-row workgroups and
@@ -1325,9 +1620,18 @@ pa_status launch_fwd(const AttnArgs& base, const pa_plan_info* plan, const int32
     bool launched = false;
     if constexpr (D <= 128) {
       if (plan->tiled_rows == PA_TILED_ROWS_WIDE) {
-        hipLaunchKernelGGL((attn_tiled_wide_kernel<D, FP8>), dim3(plan->num_tiled_items),
-                           dim3(512), 0, stream, a);
-        launched = true;
+        if constexpr (D == 128 && !FP8) {
+          if (a.bs_log2 >= 4) {
+            hipLaunchKernelGGL((attn_tiled_dma_kernel<D>), dim3(plan->num_tiled_items),
+                               dim3(512), 0, stream, a);
+            launched = true;
+          }
+        }
+        if (!launched) {
+          hipLaunchKernelGGL((attn_tiled_wide_kernel<D, FP8>), dim3(plan->num_tiled_items),
+                             dim3(512), 0, stream, a);
+          launched = true;
+        }
       }
     }
     if (!launched)
