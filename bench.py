@@ -332,18 +332,15 @@ def kernel_names(res, fp8):
         return ("prefix pass: " + kernel_names(dict(res, plan=pre, cascade_plans=None), fp8) +
                 "; suffix pass: " + kernel_names(dict(res, plan=suf, cascade_plans=None), fp8) +
                 "; merge_states_kernel")
-    p, D = res["plan"], res["wl"].D
+    p, D, BS = res["plan"], res["wl"].D, res["wl"].BS
     tag = f"<{D}{', fp8' if fp8 else ''}>"
+    dma = D == 128 and not fp8 and BS & (BS - 1) == 0    # tiles loaded into LDS by DMA
     if p["num_small_items"] and p["num_tiled_items"]:
-        k = ["attn_mixed_kernel" + tag]
+        k = ["attn_mixed_dma_kernel<128>" if dma else "attn_mixed_kernel" + tag]
     elif p["num_small_items"]:
         k = ["attn_small_kernel" + tag]
     elif p["tiled_rows"] == 256:
-        BS = res["wl"].BS
-        if D == 128 and not fp8 and BS & (BS - 1) == 0:
-            k = ["attn_tiled_dma_kernel<128>"]
-        else:
-            k = ["attn_tiled_wide_kernel" + tag]
+        k = ["attn_tiled_dma_kernel<128>" if dma else "attn_tiled_wide_kernel" + tag]
     else:
         k = ["attn_tiled_kernel" + tag]
     if p["num_reduce_items"]:

@@ -15,6 +15,9 @@
 //                              power-of-two block size: K/V tiles go from
 //                              HBM to LDS by DMA, two tiles ahead
 //   attn_mixed_kernel<D>       small-row and 128-row items in one launch
+//   attn_mixed_dma_kernel<128> the same for a bf16 cache with a power-of-two
+//                              block size, its 128-row items loading K/V
+//                              tiles into LDS by DMA (tiled_dma4_body)
 //   split_reduce_kernel<D>     LSE merge of split-KV partials (section 1.3
 //                              num_splits)
 //   merge_states_kernel        two-way LSE merge (section 6.3, step 3)
@@ -1453,6 +1456,264 @@ __global__ __launch_bounds__(512, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 }
 
 // ---------------------------------------------------------------------------
+// 4-wave LDS-DMA tiled body (128-row items of a mixed launch, bf16 cache,
+// D = 128, block size a power of two >= 16): the tile loads and layouts of
+// attn_tiled_dma_kernel, double-buffered (tile j+1 loads while tile j is
+// computed) in 64 KB, so that two workgroups still fit a compute unit beside
+// the small-row items of the same launch.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t* item, uint8_t* kreg, uint8_t* vreg) {
+  static_assert(D == 128, "4-wave LDS-DMA tiled body");
+  constexpr int NKT = D / 16, NDT = D / 32, TILE = 64 * 2 * D;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, h = lane >> 5;
+  const Item it = load_item(item);
+  const int t0 = it.t0, G = a.G, nrows = it.nrows, kv0 = it.kv0;
+  const int kv1 = min(it.kv1, a.MB * a.BS);
+  const int nt = kv1 > kv0 ? (kv1 - kv0 + 63) >> 6 : 0;
+  const float sl2 = a.scale_log2;
+
+  const int rl = wave * 32 + n;
+  const int r = it.row0 + rl;
+  const bool row_ok = rl < nrows;
+  const int tok = r / G;
+  const int head = it.kvh * G + (r - tok * G);
+  const int row_limit = a.causal ? tok + it.koff : INT_MAX;
+  const int row_lo = a.window > 0 ? tok + it.koff - (a.window - 1) : INT_MIN;
+  const int wave_limit = a.causal ? (it.row0 + wave * 32) / G + it.koff : INT_MAX;
+  const int wave_lo = a.window > 0 ? (it.row0 + wave * 32 + 31) / G + it.koff - (a.window - 1) : INT_MIN;
+  const bool wave_rows = wave * 32 < nrows;
+  const int wave_last = a.causal ? (it.row0 + min(wave * 32 + 31, nrows - 1)) / G + it.koff : INT_MAX;
+
+  bf16x8_t qf[NKT];
+  if (row_ok) {
+    const uint16_t* qp = a.q + ((int64_t)(t0 + tok) * a.H + head) * D + 8 * h;
+#pragma unroll
+    for (int t = 0; t < NKT; ++t) qf[t] = ld16(qp + 16 * t);
+  } else {
+#pragma unroll
+    for (int t = 0; t < NKT; ++t) qf[t] = zero8();
+  }
+
+  // ---- loader: the loads and LDS layouts of attn_tiled_dma_kernel; wave w
+  // (0..3) issues i = w, w + 4, w + 8, w + 12 (16-key groups 0..3), with the
+  // same row within the group (8 ((w / 2) & 1) + r8) and chunk for all four
+  const int64_t row_elems = (int64_t)a.Hkv * D;
+  const int row_bytes = (int)(row_elems * 2);
+  const int rgo = (wave >> 1) & 1, chh = wave & 1;
+  const int voff_k = (8 * rgo + (lane & 7)) * row_bytes + ((8 * chh + ((lane >> 3) ^ rgo)) << 4);
+  const int vr8 = lane >> 3;
+  const int voff_v = (8 * rgo + vr8) * row_bytes + ((8 * chh + ((lane & 7) ^ (4 * ((vr8 >> 1) & 1)))) << 4);
+  const uint8_t* cache_b = reinterpret_cast<const uint8_t*>(a.cache) + (int64_t)it.kvh * D * 2;
+  const int32_t* btrow = a.block_table + (int64_t)it.seq * a.bt_stride;
+  const int bs_log2 = a.bs_log2;
+  const int last_blk = kv1 > 0 ? (kv1 - 1) >> bs_log2 : 0;
+  const int64_t blk_bytes = (int64_t)row_bytes << bs_log2;
+  const int64_t plane_bytes = a.plane * 2;
+
+  // block-table entries of tile t: lanes 0..3 load group l's, the others a copy
+  auto fetch = [&](int t) -> int {
+    return btrow[min((kv0 + 64 * t + 16 * (lane & 3)) >> bs_log2, last_blk)];
+  };
+  // the LDS address passes through readfirstlane, so that the compiler ties
+  // no load to an LDS array and adds no wait of its own (the waits and
+  // barriers of the loop order them); the small-row body shares lds_a
+  auto dma = [&](__amdgpu_buffer_rsrc_t rs, uint8_t* dst, int voff) {
+    const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_ptr)dst);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(uintptr_t)la, 16, voff, 0, 0, 0);
+  };
+  auto load_tile = [&](int t, uint8_t* kd, uint8_t* vd, int ent) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int grp = q;
+      const int g = wave + 4 * q;
+      const int phys = __builtin_amdgcn_readlane(ent, grp);
+      const int key0 = kv0 + 64 * t + 16 * grp;
+      const bool ok = (key0 < kv1) & ((unsigned)phys < (unsigned)a.NB);
+      const int64_t x = (int64_t)phys * blk_bytes + (int64_t)(key0 & (a.BS - 1)) * row_bytes;
+      const int64_t boff = x & -(int64_t)ok;
+      const int nrec = ((min(16, kv1 - key0) - 1) * row_bytes + D * 2) & -(int)ok;
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(cache_b + boff), 0, nrec, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(cache_b + plane_bytes + boff), 0, nrec, 0x00020000);
+      dma(rk, kd + 1024 * g, voff_k);
+      dma(rv, vd + 1024 * g, voff_v);
+    }
+  };
+
+  // ---- read addresses.  K operand of k-step t, key half u (row r = n + 32u,
+  // chunk C = 2t + h): 2048 (r / 8) + 1024 (C / 8) + 128 ((C % 8) ^ ((r / 8) & 1))
+  // + 16 (r % 8) = kbase + 8192 u + 1024 (t / 4) + 256 (t % 4).  V operand of d
+  // tile dt, 16-key step ks, second half e (row 16 ks + 8 e + r8, local chunk
+  // cl of the tile's 4): vbase(dt % 2) + 4096 ks + 2048 e + 1024 (dt / 2).
+  // Both are conflict-free: the 16 lanes of a K read and the 32 lanes of a
+  // transposing read cover all 64 banks once.
+  const int n8 = n >> 3;
+  const int kbase = 2048 * n8 + 128 * (h ^ (n8 & 1)) + 16 * (n & 7);
+  const int q16 = lane >> 4, s16 = lane & 15;
+  const int r8v = 4 * h + (s16 >> 2);
+  const int clv = 2 * (q16 & 1) + ((s16 & 3) >> 1);
+  const int vbase0 = 128 * r8v + 16 * clv + 8 * (s16 & 1) + 64 * ((r8v >> 1) & 1);
+  const int vbase1 = vbase0 ^ 64;
+
+  float m_run = kNegInf, l_run = 0.f, lr_run = 0.f;
+  f32x16_t o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+
+  // (forced inline: three unrolled calls exceed the inliner's budget, and an
+  // outlined tile would keep O and the row state in scratch memory)
+  auto tile = [&](int j0, const uint8_t* kb, const uint8_t* vb, bool masked) __attribute__((always_inline)) {
+    f32x16_t s[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[u][i] = 0.f;
+#pragma unroll
+    for (int t = 0; t < NKT; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kb + kbase + 8192 * u + 1024 * (t >> 2) + 256 * (t & 3));
+        s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[t], s[u], 0, 0, 0);
+      }
+    float x[32];
+    const int lim = min(kv1 - 1, row_limit) - j0 - 4 * h;
+    const int lim_lo = (row_lo == INT_MIN) ? INT_MIN : row_lo - j0 - 4 * h;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[16 * u + i] = s[u][i];
+    if (masked) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int off = 32 * (i >> 4) + 8 * ((i & 15) >> 2) + (i & 3);
+        x[i] = (off > lim || off < lim_lo) ? kNegInf : x[i];
+      }
+    }
+    float mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, x[i]);
+    mx = max_xor<32>(mx) * sl2;
+    if (__builtin_expect(__any(mx > m_run + kRescaleSlack), 0)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+      lr_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], sl2, neg_m));
+      ps[i & 3] += x[i];
+    }
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    bf16x8_t pb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      pb[ks] = pack_bf16x8(x + 8 * ks);
+      lr_run = add_bf16x8(pb[ks], lr_run);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const uint8_t* p0 = vb + ((dt & 1) ? vbase1 : vbase0) + 4096 * ks + 1024 * (dt >> 1);
+        const bf16x8_t av = cat(lds_read_tr(reinterpret_cast<const uint16_t*>(p0)),
+                                lds_read_tr(reinterpret_cast<const uint16_t*>(p0 + 2048)));
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks], o[dt], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- double buffer: iteration j issues tile j+1's loads into the other
+  // slot after its barrier and computes tile j; the loop starts one tile
+  // early (j = -1 only issues loads)
+  int e_cur = nt > 0 ? fetch(0) : 0, e_next;   // entries of tile j+1 in iteration j
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  auto iteration = [&](auto pc, int j) {
+    constexpr int P = decltype(pc)::value & 1;    // slot of tile j
+    // this wave's loads of tile j and the lookup of tile j+1 have landed;
+    // after the barrier so have every wave's, and no wave reads tile j-1,
+    // whose slot tile j+1's loads overwrite
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    asm volatile("s_barrier" ::: "memory");
+    e_next = fetch(j + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile(j + 1, kreg + TILE * (P ^ 1), vreg + TILE * (P ^ 1), e_cur);
+    e_cur = e_next;
+    const int j0 = kv0 + 64 * j;
+    if (j >= 0 && wave_rows && j0 <= wave_last)
+      tile(j0, kreg + TILE * P, vreg + TILE * P, j0 + 64 > kv1 || j0 + 63 > wave_limit || j0 < wave_lo);
+  };
+  for (int j = nt > 0 ? -1 : 0;;) {
+    if (j >= nt) break;
+    iteration(IntC<1>{}, j++);
+    if (j >= nt) break;
+    iteration(IntC<0>{}, j++);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+
+  // ---- epilogue (as attn_tiled_kernel)
+  const float l = sum_xor<32>(l_run);
+  float lr = sum_xor<32>(lr_run);
+  if (!row_ok) return;
+  float mr = m_run, ll = l, fo = 1.f;
+  if (a.s_aux && it.prow < 0) fo = add_sink(a.s_aux[head] * kLog2e, mr, ll, lr);
+  const bool empty = !(ll > 0.f);
+  const float inv = empty ? 0.f : fo / lr;
+  const float lse_v = empty ? kNegInf : (mr + __log2f(ll)) * kLn2;
+  if (it.prow < 0) {
+    const int64_t orow = (int64_t)(t0 + tok) * a.H + head;
+    uint16_t* op = a.out + orow * D + 4 * h;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) {
+        uint2 w;
+        w.x = pack_bf16x2(o[dt][4 * ig] * inv, o[dt][4 * ig + 1] * inv);
+        w.y = pack_bf16x2(o[dt][4 * ig + 2] * inv, o[dt][4 * ig + 3] * inv);
+        *reinterpret_cast<uint2*>(op + 32 * dt + 8 * ig) = w;
+      }
+    if (h == 0 && a.lse) a.lse[orow] = lse_v;
+  } else {
+    float* pp = a.part_o + (int64_t)(it.prow + rl) * D + 4 * h;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig)
+        *reinterpret_cast<f32x4_t*>(pp + 32 * dt + 8 * ig) =
+            f32x4_t{o[dt][4 * ig] * inv, o[dt][4 * ig + 1] * inv, o[dt][4 * ig + 2] * inv,
+                    o[dt][4 * ig + 3] * inv};
+    if (h == 0) a.part_lse[it.prow + rl] = lse_v;
+  }
+}
+
+// Mixed launch of a bf16 cache at D = 128 with a power-of-two block size:
+// small-row items as in attn_mixed_kernel, tiled items by the 4-wave LDS-DMA
+// body.  The small body's staging area and the K slots share lds_a.
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_mixed_dma_kernel(AttnArgs a) {
+  constexpr int TILE = 64 * 2 * D;
+  constexpr int LA = small_lds_bytes<D>() > 2 * TILE ? small_lds_bytes<D>() : 2 * TILE;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_a[(LA + 1023) / 1024 * 1024];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_b[2 * TILE];
+  const int32_t* item = a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS;
+  if (ld_uniform(item + 7))
+    tiled_dma4_body<D>(a, item, lds_a, lds_b);
+  else
+    small_body<D, false, SmallCfg<D>::PF>(a, item, lds_a);
+}
+
+// ---------------------------------------------------------------------------
 // Mixed launch: when a batch has both decode-like and prefill rows, one grid
 // runs both kinds of item (word 7 of an item: 0 small-row, 1 tiled), in the
 // planner's longest-first order, so the HBM-bound small-row workgroups and
@@ -1612,8 +1873,17 @@ pa_status launch_fwd(const AttnArgs& base, const pa_plan_info* plan, const int32
   AttnArgs a = base;
   a.items = items;
   if (plan->num_small_items > 0 && plan->num_tiled_items > 0) {
-    hipLaunchKernelGGL((attn_mixed_kernel<D, FP8>),
-                       dim3(plan->num_small_items + plan->num_tiled_items), dim3(256), 0, stream, a);
+    bool launched = false;
+    if constexpr (D == 128 && !FP8) {
+      if (a.bs_log2 >= 4) {
+        hipLaunchKernelGGL((attn_mixed_dma_kernel<D>),
+                           dim3(plan->num_small_items + plan->num_tiled_items), dim3(256), 0, stream, a);
+        launched = true;
+      }
+    }
+    if (!launched)
+      hipLaunchKernelGGL((attn_mixed_kernel<D, FP8>),
+                         dim3(plan->num_small_items + plan->num_tiled_items), dim3(256), 0, stream, a);
   } else if (plan->num_small_items > 0) {
     hipLaunchKernelGGL((attn_small_kernel<D, FP8>), dim3(plan->num_small_items), dim3(256), 0, stream, a);
   } else if (plan->num_tiled_items > 0) {

@@ -1,5 +1,5 @@
-"""The LDS layouts of attn_tiled_dma_kernel<128> (paged_kv_varlen_flash_amd/
-csrc/pagedattn.hip), modelled on the CPU: the index formulas of its loader
+"""The LDS layouts of attn_tiled_dma_kernel<128> and tiled_dma4_body
+(paged_kv_varlen_flash_amd/csrc/pagedattn.hip), modelled on the CPU: the index formulas of its loader
 and of its operand reads, restated here, must put every (key row, 16-byte
 chunk) of a 64-key tile in LDS exactly once, give each MFMA operand read the
 elements that the row-major layout of attn_tiled_kernel gives it, and hit
@@ -10,16 +10,17 @@ D = 128
 ROW_BYTES_CASES = (256, 1024, 4096)   # Hkv * D * 2 for Hkv = 1, 4, 16
 
 
-def loader(row_bytes):
-    """{LDS byte offset: (row, chunk)} of the K and V planes: wave w issues
-    loads i = w and w + 8 of each plane; lane l writes 16 bytes at 1024 i + 16 l
-    with the chunk its voffset selects."""
+def loader(row_bytes, waves=8):
+    """{LDS byte offset: (row, chunk)} of the K and V planes.  8 waves
+    (attn_tiled_dma_kernel): wave w issues loads i = w and w + 8 of each plane;
+    4 waves (tiled_dma4_body): i = w, w + 4, w + 8, w + 12.  Lane l writes 16
+    bytes at 1024 i + 16 l with the chunk its voffset selects."""
     K, V = {}, {}
-    for w in range(8):
+    for w in range(waves):
         rgo, chh = (w >> 1) & 1, w & 1
-        for q in range(2):
-            grp = (w >> 2) + 2 * q           # 16-key group of the load
-            g = w + 8 * q
+        for q in range(16 // waves):
+            grp = (w >> 2) + 2 * q if waves == 8 else q   # 16-key group of the load
+            g = w + waves * q
             for l in range(64):
                 voff_k = (8 * rgo + (l & 7)) * row_bytes + ((8 * chh + ((l >> 3) ^ rgo)) << 4)
                 r8 = l >> 3
@@ -47,16 +48,18 @@ def v_read(lane, dt, ks, e):
     return (vb0 ^ 64 if dt & 1 else vb0) + 4096 * ks + 2048 * e + 1024 * (dt >> 1)
 
 
+@pytest.mark.parametrize("waves", (8, 4))
 @pytest.mark.parametrize("row_bytes", ROW_BYTES_CASES)
-def test_every_chunk_once(row_bytes):
-    K, V = loader(row_bytes)
+def test_every_chunk_once(row_bytes, waves):
+    K, V = loader(row_bytes, waves)
     full = sorted((r, c) for r in range(64) for c in range(16))
     assert sorted(K.values()) == full and sorted(V.values()) == full
 
 
+@pytest.mark.parametrize("waves", (8, 4))
 @pytest.mark.parametrize("row_bytes", ROW_BYTES_CASES)
-def test_operand_reads_match_row_major(row_bytes):
-    K, V = loader(row_bytes)
+def test_operand_reads_match_row_major(row_bytes, waves):
+    K, V = loader(row_bytes, waves)
     for lane in range(64):
         n, h = lane & 31, lane >> 5
         q16, s16 = lane >> 4, lane & 15
