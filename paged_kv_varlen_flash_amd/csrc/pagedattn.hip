@@ -18,6 +18,7 @@
 //   attn_mixed_dma_kernel<128> the same for a bf16 cache with a power-of-two
 //                              block size, its 128-row items loading K/V
 //                              tiles into LDS by DMA (tiled_dma4_body)
+//   attn_tiled_dma4_kernel<128> 128-row items alone, by tiled_dma4_body
 //   split_reduce_kernel<D>     LSE merge of split-KV partials (section 1.3
 //                              num_splits)
 //   merge_states_kernel        two-way LSE merge (section 6.3, step 3)
@@ -1193,6 +1194,44 @@ struct IntC {
 // s_waitcnt with only the vector-memory count bounded (gfx9 encoding)
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// Stores one wave's 32 rows of O (lane (n, h) holds, in o[dt][4 ig + e],
+// O^T[d = 32 dt + 8 ig + 4 h + e][row n], already normalised) through an
+// 8 KB LDS region that no other wave touches: the 8-byte pieces go in with
+// their 16-byte chunk index XORed by n mod 16, and come back 16 bytes per
+// lane, 4 whole rows per instruction, so each wave issues 8 stores of whole
+// 256-byte rows instead of 16 scattered 8-byte ones.  Rows at or past
+// nrows_left are not stored.
+template <int NDT>
+__device__ __forceinline__ void store_rows_staged(const f32x16_t* o, float inv, uint8_t* stage,
+                                                  int lane, uint16_t* out, int H, int t0,
+                                                  int row0, int nrows_left, int G, int kvh) {
+  constexpr int D = 32 * NDT;
+  static_assert(D == 128, "16 chunks of 16 bytes per row");
+  const int n = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int ig = 0; ig < 4; ++ig) {
+      uint2 w;
+      w.x = pack_bf16x2(o[dt][4 * ig] * inv, o[dt][4 * ig + 1] * inv);
+      w.y = pack_bf16x2(o[dt][4 * ig + 2] * inv, o[dt][4 * ig + 3] * inv);
+      const int c = 4 * dt + ig;
+      *reinterpret_cast<uint2*>(stage + n * 256 + ((c ^ (n & 15)) << 4) + 8 * h) = w;
+    }
+  const int c = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int lr = 4 * i + (lane >> 4);
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + lr * 256 + ((c ^ (lr & 15)) << 4));
+    if (lr < nrows_left) {
+      const int r = row0 + lr;
+      const int tok = r / G;
+      const int head = kvh * G + (r - tok * G);
+      *reinterpret_cast<u32x4_t*>(out + ((int64_t)(t0 + tok) * H + head) * D + 8 * c) = v;
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(512, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_tiled_dma_kernel(AttnArgs a) {
   static_assert(D == 128, "LDS-DMA tiled kernel");
@@ -1273,6 +1312,13 @@ __global__ __launch_bounds__(512, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   auto fetch = [&](int t) -> int {
     return btrow[min((kv0 + 64 * t + 16 * (lane & 3)) >> bs_log2, last_blk)];
   };
+  // the LDS address passes through readfirstlane, so that the compiler ties
+  // no load to an LDS array and adds no wait of its own (the waits and
+  // barriers of the loop order the loads and the reads)
+  auto dma = [&](__amdgpu_buffer_rsrc_t rs, uint8_t* dst, int voff) {
+    const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_ptr)dst);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(uintptr_t)la, 16, voff, 0, 0, 0);
+  };
   auto load_tile = [&](int t, uint8_t* kd, uint8_t* vd, int ent) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -1288,8 +1334,8 @@ __global__ __launch_bounds__(512, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
           const_cast<uint8_t*>(cache_b + boff), 0, nrec, 0x00020000);
       const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint8_t*>(cache_b + plane_bytes + boff), 0, nrec, 0x00020000);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_ptr)(kd + 1024 * g), 16, voff_k, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_ptr)(vd + 1024 * g), 16, voff_v, 0, 0, 0);
+      dma(rk, kd + 1024 * g, voff_k);
+      dma(rv, vd + 1024 * g, voff_v);
     }
   };
   constexpr int kLoadsPerTile = 4;
@@ -1385,26 +1431,28 @@ __global__ __launch_bounds__(512, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   };
 
   // ---- the loop starts two tiles early (j = -2, -1 only issue loads), so
-  // that no load is in flight on entry: every load is then issued by the
-  // same unrolled code, which keeps the compiler's own wait counts exact.
-  // The lookup of tile 0 and the Q loads land before the loop.
-  int e_cur = nt > 0 ? fetch(0) : 0, e_next;   // entries of tile j+2 at the top of iteration j
+  // that the first tiles load as the later ones do; loads and lookups stop at
+  // the last tile.  The lookup of tile 0 and the Q loads land before the loop.
+  int e_cur = nt > 0 ? fetch(0) : 0, e_next = 0;   // entries of tile j+2 at the top of iteration j
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   auto iteration = [&](auto pc, int j) {
     constexpr int P = decltype(pc)::value;    // slot of tile j (j mod 3)
     // tile j and tile j+2's entries have landed (only tile j+1's loads may
-    // be in flight); after the barrier every wave is done with tile j-1,
-    // whose slots tile j+2's loads overwrite
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoadsPerTile));
+    // be in flight, and none past the last tile); after the barrier every
+    // wave is done with tile j-1, whose slots tile j+2's loads overwrite
+    if (j + 1 < nt)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoadsPerTile));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     // a workgroup barrier with no memory fence: a fence would wait for every
     // LDS-DMA load in flight, tile j+1's too ("memory" keeps the compiler
     // from moving LDS accesses across it)
     asm volatile("s_barrier" ::: "memory");
-    e_next = fetch(j + 3);
+    if (j + 3 < nt) e_next = fetch(j + 3);
     // the lookup goes out before the tile's loads, so that waiting for it
     // never waits for them
     __builtin_amdgcn_sched_barrier(0);
-    load_tile(j + 2, kslot(IntC<P + 2>{}), vslot(IntC<P + 2>{}), e_cur);
+    if (j + 2 < nt) load_tile(j + 2, kslot(IntC<P + 2>{}), vslot(IntC<P + 2>{}), e_cur);
     e_cur = e_next;
     const int j0 = kv0 + 64 * j;
     if (j >= 0 && wave_rows && j0 <= wave_last)
@@ -1420,29 +1468,25 @@ __global__ __launch_bounds__(512, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
-  // ---- epilogue (as attn_tiled_kernel)
+  // ---- epilogue (as attn_tiled_kernel; whole outputs go through LDS)
   const float l = sum_xor<32>(l_run);
   float lr = sum_xor<32>(lr_run);
-  if (!row_ok) return;
   float mr = m_run, ll = l, fo = 1.f;
-  if (a.s_aux && it.prow < 0) fo = add_sink(a.s_aux[head] * kLog2e, mr, ll, lr);
+  if (a.s_aux && it.prow < 0 && row_ok) fo = add_sink(a.s_aux[head] * kLog2e, mr, ll, lr);
   const bool empty = !(ll > 0.f);
   const float inv = empty ? 0.f : fo / lr;
   const float lse_v = empty ? kNegInf : (mr + __log2f(ll)) * kLn2;
   if (it.prow < 0) {
-    const int64_t orow = (int64_t)(t0 + tok) * a.H + head;
-    uint16_t* op = a.out + orow * D + 4 * h;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int ig = 0; ig < 4; ++ig) {
-        uint2 w;
-        w.x = pack_bf16x2(o[dt][4 * ig] * inv, o[dt][4 * ig + 1] * inv);
-        w.y = pack_bf16x2(o[dt][4 * ig + 2] * inv, o[dt][4 * ig + 3] * inv);
-        *reinterpret_cast<uint2*>(op + 32 * dt + 8 * ig) = w;
-      }
-    if (h == 0 && a.lse) a.lse[orow] = lse_v;
+    // the slots of tiles nt and nt+1 hold nothing and no load is in flight
+    // (loads stop at the last tile, and after the last barrier no wave reads
+    // them): 64 KB, 8 KB per wave
+    const int s = (nt + ((wave >> 1) & 1)) % 3;
+    uint8_t* region = wave < 4 ? (s == 0 ? ks0 : s == 1 ? ks1 : ks2) : (s == 0 ? vs0 : s == 1 ? vs1 : vs2);
+    store_rows_staged<NDT>(o, inv, region + 8192 * (wave & 1), lane, a.out, a.H, t0,
+                           it.row0 + wave * 32, nrows - wave * 32, G, it.kvh);
+    if (h == 0 && a.lse && row_ok) a.lse[(int64_t)(t0 + tok) * a.H + head] = lse_v;
   } else {
+    if (!row_ok) return;
     float* pp = a.part_o + (int64_t)(it.prow + rl) * D + 4 * h;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -1462,7 +1506,7 @@ __global__ __launch_bounds__(512, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 // computed) in 64 KB, so that two workgroups still fit a compute unit beside
 // the small-row items of the same launch.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool STAGED>
 __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t* item, uint8_t* kreg, uint8_t* vreg) {
   static_assert(D == 128, "4-wave LDS-DMA tiled body");
   constexpr int NKT = D / 16, NDT = D / 32, TILE = 64 * 2 * D;
@@ -1637,18 +1681,20 @@ __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t
   // ---- double buffer: iteration j issues tile j+1's loads into the other
   // slot after its barrier and computes tile j; the loop starts one tile
   // early (j = -1 only issues loads)
-  int e_cur = nt > 0 ? fetch(0) : 0, e_next;   // entries of tile j+1 in iteration j
+  int e_cur = nt > 0 ? fetch(0) : 0, e_next = 0;   // entries of tile j+1 in iteration j
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   auto iteration = [&](auto pc, int j) {
     constexpr int P = decltype(pc)::value & 1;    // slot of tile j
     // this wave's loads of tile j and the lookup of tile j+1 have landed;
     // after the barrier so have every wave's, and no wave reads tile j-1,
-    // whose slot tile j+1's loads overwrite
+    // whose slot tile j+1's loads overwrite.  With STAGED, loads stop at the
+    // last tile, so that the epilogue finds the other slot empty; without,
+    // they run on, zero-filled (measured 1 % faster in mixed launches)
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     asm volatile("s_barrier" ::: "memory");
-    e_next = fetch(j + 2);
+    if (!STAGED || j + 2 < nt) e_next = fetch(j + 2);
     __builtin_amdgcn_sched_barrier(0);
-    load_tile(j + 1, kreg + TILE * (P ^ 1), vreg + TILE * (P ^ 1), e_cur);
+    if (!STAGED || j + 1 < nt) load_tile(j + 1, kreg + TILE * (P ^ 1), vreg + TILE * (P ^ 1), e_cur);
     e_cur = e_next;
     const int j0 = kv0 + 64 * j;
     if (j >= 0 && wave_rows && j0 <= wave_last)
@@ -1662,16 +1708,24 @@ __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
-  // ---- epilogue (as attn_tiled_kernel)
+  // ---- epilogue (as attn_tiled_kernel; whole outputs go through LDS)
   const float l = sum_xor<32>(l_run);
   float lr = sum_xor<32>(lr_run);
-  if (!row_ok) return;
   float mr = m_run, ll = l, fo = 1.f;
-  if (a.s_aux && it.prow < 0) fo = add_sink(a.s_aux[head] * kLog2e, mr, ll, lr);
+  if (a.s_aux && it.prow < 0 && row_ok) fo = add_sink(a.s_aux[head] * kLog2e, mr, ll, lr);
   const bool empty = !(ll > 0.f);
   const float inv = empty ? 0.f : fo / lr;
   const float lse_v = empty ? kNegInf : (mr + __log2f(ll)) * kLn2;
-  if (it.prow < 0) {
+  if (STAGED && it.prow < 0) {
+    // the slot of tile nt holds nothing and no load is in flight (loads stop
+    // at the last tile, and after the last barrier no wave reads it): 32 KB,
+    // 8 KB per wave
+    uint8_t* region = (wave < 2 ? kreg : vreg) + TILE * (nt & 1) + 8192 * (wave & 1);
+    store_rows_staged<NDT>(o, inv, region, lane, a.out, a.H, t0, it.row0 + wave * 32,
+                           nrows - wave * 32, G, it.kvh);
+    if (h == 0 && a.lse && row_ok) a.lse[(int64_t)(t0 + tok) * a.H + head] = lse_v;
+  } else if (it.prow < 0) {
+    if (!row_ok) return;
     const int64_t orow = (int64_t)(t0 + tok) * a.H + head;
     uint16_t* op = a.out + orow * D + 4 * h;
 #pragma unroll
@@ -1685,6 +1739,7 @@ __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t
       }
     if (h == 0 && a.lse) a.lse[orow] = lse_v;
   } else {
+    if (!row_ok) return;
     float* pp = a.part_o + (int64_t)(it.prow + rl) * D + 4 * h;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -1695,6 +1750,20 @@ __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t
                     o[dt][4 * ig + 3] * inv};
     if (h == 0) a.part_lse[it.prow + rl] = lse_v;
   }
+}
+
+// 128-row tiled items alone (bf16 cache, D = 128, power-of-two block size):
+// two 4-wave workgroups per compute unit, each double-buffering its tiles,
+// so that one workgroup's first loads and last stores overlap the other's
+// tiles.  Measured on the mix's 8 prefills (592-1811 tokens): 141-144 us
+// against 146-147 us for 256-row blocks in attn_tiled_dma_kernel; on 4 x 8192
+// tokens 2435-2464 us against 2395-2402 us, so long prefills keep 256 rows.
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_tiled_dma4_kernel(AttnArgs a) {
+  constexpr int TILE = 64 * 2 * D;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_a[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_b[2 * TILE];
+  tiled_dma4_body<D, true>(a, a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS, lds_a, lds_b);
 }
 
 // Mixed launch of a bf16 cache at D = 128 with a power-of-two block size:
@@ -1708,7 +1777,9 @@ __global__ __launch_bounds__(256, 2) void attn_mixed_dma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_b[2 * TILE];
   const int32_t* item = a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS;
   if (ld_uniform(item + 7))
-    tiled_dma4_body<D>(a, item, lds_a, lds_b);
+    // (loads through the last tile pair and outputs stored directly: the
+    // staged form measured 1 % slower here)
+    tiled_dma4_body<D, false>(a, item, lds_a, lds_b);
   else
     small_body<D, false, SmallCfg<D>::PF>(a, item, lds_a);
 }
@@ -1902,6 +1973,13 @@ pa_status launch_fwd(const AttnArgs& base, const pa_plan_info* plan, const int32
                              dim3(512), 0, stream, a);
           launched = true;
         }
+      }
+    }
+    if constexpr (D == 128 && !FP8) {
+      if (!launched && a.bs_log2 >= 4) {
+        hipLaunchKernelGGL((attn_tiled_dma4_kernel<D>), dim3(plan->num_tiled_items), dim3(256), 0,
+                           stream, a);
+        launched = true;
       }
     }
     if (!launched)

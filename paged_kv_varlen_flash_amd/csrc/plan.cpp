@@ -270,17 +270,15 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
   thread_local std::vector<Unit> units;
   units.clear();
   // Tiled row blocks: PA_TILED_ROWS_WIDE rows (8-wave workgroups sharing each
-  // K/V tile) when no sequence is small-row, D <= 128, and either the
-  // prefills are long (2048 query tokens or more on average), or D = 64, or
-  // the LDS-DMA kernel runs them (D = 128, bf16 cache, power-of-two block
-  // size) and there is at least one 256-row block per compute unit; else
-  // PA_TILED_ROWS (4-wave workgroups, which a mixed launch shares with
-  // small-row items).  Measured on MI355X (H = 32, Hkv = 8, causal): 256-row
-  // blocks took 5-9 % less time for prefills of 2048-8192 tokens and 3 % less
-  // at D = 64 for 256-2048 tokens; at D = 128 for 592-1811 tokens they took
-  // 3 % more with register-staged loads and 2-4 % less with the LDS-DMA kernel.
+  // K/V tile) when no sequence is small-row, D <= 128, and the prefills are
+  // long (2048 query tokens or more on average) or D = 64; else PA_TILED_ROWS
+  // (4-wave workgroups, which a mixed launch shares with small-row items).
+  // Measured on MI355X (H = 32, Hkv = 8, causal): 256-row blocks took 4-9 %
+  // less time for prefills of 2048-8192 tokens and 3 % less at D = 64 for
+  // 256-2048 tokens, but 2-3 % more at D = 128 for 592-1811 tokens (with DMA
+  // tile loads in both kernels, as with register-staged loads).
   bool any_small = false;
-  int64_t tiled_q = 0, tiled_seqs = 0, wide_blocks = 0;
+  int64_t tiled_q = 0, tiled_seqs = 0;
   for (int32_t b = 0; b < B; ++b) {
     const int32_t Lq = cu[b + 1] - cu[b];
     if (Lq == 0) continue;
@@ -289,16 +287,10 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
     } else {
       tiled_q += Lq;
       ++tiled_seqs;
-      wide_blocks += ((int64_t)Lq * G + PA_TILED_ROWS_WIDE - 1) / PA_TILED_ROWS_WIDE * Hkv;
     }
   }
-  // compute units to fill: the caller's device, or one whole MI355X
-  const int64_t target = p->num_cus > 0 ? p->num_cus : PA_PLAN_TARGET_CUS;
-  const bool dma_kernel = p->head_size == 128 && !p->kv_cache_fp8 &&
-                          (p->block_size & (p->block_size - 1)) == 0;
   const bool wide = !any_small && tiled_seqs > 0 && p->head_size <= 128 &&
-                    (p->head_size <= 64 || tiled_q >= 2048 * tiled_seqs ||
-                     (dma_kernel && wide_blocks >= target));
+                    (p->head_size <= 64 || tiled_q >= 2048 * tiled_seqs);
   const int32_t tiled_rows = wide ? PA_TILED_ROWS_WIDE : PA_TILED_ROWS;
   for (int32_t b = 0; b < B; ++b) {
     const int32_t Lq = cu[b + 1] - cu[b], Lk = sk[b];
@@ -334,6 +326,8 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
     if (u.small) { small_keys += u.kv_end - u.kv_begin; ++n_small; }
     else { tiled_keys += u.kv_end - u.kv_begin; ++n_tiled; }
   }
+  // compute units to fill: the caller's device, or one whole MI355X
+  const int64_t target = p->num_cus > 0 ? p->num_cus : PA_PLAN_TARGET_CUS;
   int64_t tiled_chunk = 0;
   // tiled rows (bound by the matrix cores): split only when there are too
   // few blocks to fill the chip; cuts fall on whole key tiles

@@ -615,29 +615,23 @@ def test_num_cus(L):
 
 
 def test_wide_rows_rule(L):
-    """Prefill-only plans use 256-row blocks when the prefills are long, at
-    D = 64, or when the LDS-DMA kernel runs them (D = 128, bf16 cache,
-    power-of-two block size) with at least one block per compute unit; the
-    8 prefills of chunked_prefill_mix (592-1811 tokens) qualify on the last
-    count with 256 compute units, not with 2048."""
-    wl = W.make("chunked_prefill_mix_prefill", materialise=False)
-    def rows(bs=wl.BS, fp8=False, cus=0, d=wl.D):
-        p = ops.make_params(wl.B, wl.H, wl.Hkv, d, bs, -(-wl.num_blocks * wl.BS // bs),
+    """Prefill-only plans use 256-row blocks at D = 64 or when the prefills
+    average 2048 query tokens or more, whatever the block size or cache
+    format; the 8 prefills of chunked_prefill_mix (592-1811 tokens) keep
+    128-row blocks, and a plan with decode rows always does."""
+    def rows(name, bs=None, fp8=False, d=None):
+        wl = W.make(name, materialise=False)
+        bs = bs or wl.BS
+        p = ops.make_params(wl.B, wl.H, wl.Hkv, d or wl.D, bs, -(-wl.num_blocks * wl.BS // bs),
                             -(-wl.block_table.shape[1] * wl.BS // bs), True, wl.scale,
-                            kv_cache_fp8=fp8, num_cus=cus)
+                            kv_cache_fp8=fp8)
         return ops.pa_plan_varlen(p, wl.cu_seqlens_q, wl.k_lens)[1].tiled_rows
-    q = np.diff(wl.cu_seqlens_q)
-    G = wl.H // wl.Hkv
-    blocks = int(sum(-(-int(x) * G // 256) for x in q)) * wl.Hkv
-    assert 256 <= blocks < 2048 and q.mean() < 2048
-    assert rows() == ops.PA_TILED_ROWS_WIDE                  # BS = 32
-    assert rows(bs=64) == ops.PA_TILED_ROWS_WIDE
-    assert rows(bs=48) == ops.PA_TILED_ROWS                  # not a power of two
-    assert rows(fp8=True) == ops.PA_TILED_ROWS               # E4M3 cache
-    assert rows(cus=2048) == ops.PA_TILED_ROWS               # fewer blocks than units
-    assert rows(cus=blocks) == ops.PA_TILED_ROWS_WIDE
-    assert rows(cus=blocks + 1) == ops.PA_TILED_ROWS
-    assert rows(d=64) == ops.PA_TILED_ROWS_WIDE              # D = 64: always
+    short, long_ = "chunked_prefill_mix_prefill", "prefill_causal_8k"
+    for kw in ({}, {"bs": 64}, {"bs": 48}, {"fp8": True}):
+        assert rows(short, **kw) == ops.PA_TILED_ROWS
+        assert rows(long_, **kw) == ops.PA_TILED_ROWS_WIDE
+    assert rows(short, d=64) == ops.PA_TILED_ROWS_WIDE
+    assert rows("chunked_prefill_mix") == ops.PA_TILED_ROWS
 
 
 def test_binding_checks_fwd_shapes():

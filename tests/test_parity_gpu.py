@@ -220,12 +220,8 @@ def test_prefill_only(case):
         f"force={force}")
     plan = _check_case(spec, np.random.default_rng(7000 + case), force, f"prefill_only{case}")
     assert plan.info.num_small_items == 0 and plan.info.num_tiled_items > 0
-    # 256-row blocks (8-wave workgroups) at D = 64, for long prefills at
-    # D = 128, or at D = 128 with a power-of-two block size (LDS-DMA kernel)
-    # and a block per compute unit
-    blocks = Hkv * sum(-(-q * G // 256) for q, _ in seqs)
-    wide = (D <= 64 or (D <= 128 and np.mean([q for q, _ in seqs]) >= 2048) or
-            (D == 128 and BS & (BS - 1) == 0 and blocks >= 256))
+    # 256-row blocks (8-wave workgroups) at D = 64, or for long prefills at D = 128
+    wide = D <= 64 or (D <= 128 and np.mean([q for q, _ in seqs]) >= 2048)
     assert plan.info.tiled_rows == (256 if wide else 128)
 
 
