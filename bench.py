@@ -415,6 +415,10 @@ def mixed_entry(res, fp8, tkey):
                       "traffic": (tr["read_bytes"] + tr["write_bytes"]) if tr else None,
                       "traffic_read_over_algorithmic": (round(tr["read_bytes"] / res["kv_bytes"], 4)
                                                         if tr else None),
+                      # the same with the queries (read once) counted as algorithmic
+                      "traffic_read_over_kv_and_q": (
+                          round(tr["read_bytes"] / (res["kv_bytes"] + tr["q_bytes"]), 4)
+                          if tr and "q_bytes" in tr else None),
                       "kernel": "pa_varlen_fwd%s: %s" % ("_fp8" if fp8 else "",
                                                          kernel_names(res, fp8)),
                       "per_launch_flops": res["flops"], "per_launch_bytes": res["kv_bytes"],
