@@ -1194,6 +1194,15 @@ struct IntC {
 // s_waitcnt with only the vector-memory count bounded (gfx9 encoding)
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// Block-table entries of one 64-key tile's four 16-key groups, read by
+// scalar loads: their waits count on lgkmcnt, which nothing else holds at
+// the top of a tile iteration (the previous tile's LDS reads have all been
+// consumed), so waiting for them never waits for a tile load in flight.
+struct TileEntries {
+  int e0, e1, e2, e3;
+  __device__ int get(int g) const { return g == 0 ? e0 : g == 1 ? e1 : g == 2 ? e2 : e3; }
+};
+
 // Stores one wave's 32 rows of O (lane (n, h) holds, in o[dt][4 ig + e],
 // O^T[d = 32 dt + 8 ig + 4 h + e][row n], already normalised) through an
 // 8 KB LDS region that no other wave touches: the 8-byte pieces go in with
@@ -1308,9 +1317,14 @@ __global__ __launch_bounds__(512, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const int64_t blk_bytes = (int64_t)row_bytes << bs_log2;
   const int64_t plane_bytes = a.plane * 2;
   const int grp0 = wave >> 2;              // the wave's two groups: grp0 and grp0 + 2
-  // block-table entries of tile t: lanes 0..3 load group l's, the others a copy
-  auto fetch = [&](int t) -> int {
-    return btrow[min((kv0 + 64 * t + 16 * (lane & 3)) >> bs_log2, last_blk)];
+  // block-table entries of tile t's four 16-key groups (clamped to the
+  // range's last block)
+  auto fetch = [&](int t) -> TileEntries {
+    const int k0 = kv0 + 64 * t;
+    return TileEntries{ld_uniform(btrow + min(k0 >> bs_log2, last_blk)),
+                       ld_uniform(btrow + min((k0 + 16) >> bs_log2, last_blk)),
+                       ld_uniform(btrow + min((k0 + 32) >> bs_log2, last_blk)),
+                       ld_uniform(btrow + min((k0 + 48) >> bs_log2, last_blk))};
   };
   // the LDS address passes through readfirstlane, so that the compiler ties
   // no load to an LDS array and adds no wait of its own (the waits and
@@ -1319,12 +1333,12 @@ __global__ __launch_bounds__(512, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_ptr)dst);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(uintptr_t)la, 16, voff, 0, 0, 0);
   };
-  auto load_tile = [&](int t, uint8_t* kd, uint8_t* vd, int ent) {
+  auto load_tile = [&](int t, uint8_t* kd, uint8_t* vd, const TileEntries& ent) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int grp = grp0 + 2 * q;
       const int g = wave + 8 * q;
-      const int phys = __builtin_amdgcn_readlane(ent, grp);
+      const int phys = ent.get(grp);
       const int key0 = kv0 + 64 * t + 16 * grp;
       const bool ok = (key0 < kv1) & ((unsigned)phys < (unsigned)a.NB);
       const int64_t x = (int64_t)phys * blk_bytes + (int64_t)(key0 & (a.BS - 1)) * row_bytes;
@@ -1433,13 +1447,14 @@ __global__ __launch_bounds__(512, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   // ---- the loop starts two tiles early (j = -2, -1 only issue loads), so
   // that the first tiles load as the later ones do; loads and lookups stop at
   // the last tile.  The lookup of tile 0 and the Q loads land before the loop.
-  int e_cur = nt > 0 ? fetch(0) : 0, e_next = 0;   // entries of tile j+2 at the top of iteration j
+  TileEntries e_cur = nt > 0 ? fetch(0) : TileEntries{0, 0, 0, 0};   // entries of tile j+2 at the top of iteration j
+  TileEntries e_next = e_cur;
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   auto iteration = [&](auto pc, int j) {
     constexpr int P = decltype(pc)::value;    // slot of tile j (j mod 3)
-    // tile j and tile j+2's entries have landed (only tile j+1's loads may
-    // be in flight, and none past the last tile); after the barrier every
-    // wave is done with tile j-1, whose slots tile j+2's loads overwrite
+    // tile j has landed (only tile j+1's loads may be in flight, and none
+    // past the last tile); after the barrier every wave is done with tile
+    // j-1, whose slots tile j+2's loads overwrite
     if (j + 1 < nt)
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoadsPerTile));
     else
@@ -1449,8 +1464,6 @@ __global__ __launch_bounds__(512, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     // from moving LDS accesses across it)
     asm volatile("s_barrier" ::: "memory");
     if (j + 3 < nt) e_next = fetch(j + 3);
-    // the lookup goes out before the tile's loads, so that waiting for it
-    // never waits for them
     __builtin_amdgcn_sched_barrier(0);
     if (j + 2 < nt) load_tile(j + 2, kslot(IntC<P + 2>{}), vslot(IntC<P + 2>{}), e_cur);
     e_cur = e_next;
@@ -1557,9 +1570,14 @@ __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t
   const int64_t blk_bytes = (int64_t)row_bytes << bs_log2;
   const int64_t plane_bytes = a.plane * 2;
 
-  // block-table entries of tile t: lanes 0..3 load group l's, the others a copy
-  auto fetch = [&](int t) -> int {
-    return btrow[min((kv0 + 64 * t + 16 * (lane & 3)) >> bs_log2, last_blk)];
+  // block-table entries of tile t's four 16-key groups (clamped to the
+  // range's last block)
+  auto fetch = [&](int t) -> TileEntries {
+    const int k0 = kv0 + 64 * t;
+    return TileEntries{ld_uniform(btrow + min(k0 >> bs_log2, last_blk)),
+                       ld_uniform(btrow + min((k0 + 16) >> bs_log2, last_blk)),
+                       ld_uniform(btrow + min((k0 + 32) >> bs_log2, last_blk)),
+                       ld_uniform(btrow + min((k0 + 48) >> bs_log2, last_blk))};
   };
   // the LDS address passes through readfirstlane, so that the compiler ties
   // no load to an LDS array and adds no wait of its own (the waits and
@@ -1568,12 +1586,12 @@ __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t
     const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_ptr)dst);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(uintptr_t)la, 16, voff, 0, 0, 0);
   };
-  auto load_tile = [&](int t, uint8_t* kd, uint8_t* vd, int ent) {
+  auto load_tile = [&](int t, uint8_t* kd, uint8_t* vd, const TileEntries& ent) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int grp = q;
       const int g = wave + 4 * q;
-      const int phys = __builtin_amdgcn_readlane(ent, grp);
+      const int phys = ent.get(grp);
       const int key0 = kv0 + 64 * t + 16 * grp;
       const bool ok = (key0 < kv1) & ((unsigned)phys < (unsigned)a.NB);
       const int64_t x = (int64_t)phys * blk_bytes + (int64_t)(key0 & (a.BS - 1)) * row_bytes;
@@ -1681,7 +1699,8 @@ __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t
   // ---- double buffer: iteration j issues tile j+1's loads into the other
   // slot after its barrier and computes tile j; the loop starts one tile
   // early (j = -1 only issues loads)
-  int e_cur = nt > 0 ? fetch(0) : 0, e_next = 0;   // entries of tile j+1 in iteration j
+  TileEntries e_cur = nt > 0 ? fetch(0) : TileEntries{0, 0, 0, 0};   // entries of tile j+1 in iteration j
+  TileEntries e_next = e_cur;
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   auto iteration = [&](auto pc, int j) {
     constexpr int P = decltype(pc)::value & 1;    // slot of tile j
