@@ -1519,7 +1519,7 @@ __global__ __launch_bounds__(512, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 // computed) in 64 KB, so that two workgroups still fit a compute unit beside
 // the small-row items of the same launch.
 // ---------------------------------------------------------------------------
-template <int D, bool STAGED>
+template <int D>
 __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t* item, uint8_t* kreg, uint8_t* vreg) {
   static_assert(D == 128, "4-wave LDS-DMA tiled body");
   constexpr int NKT = D / 16, NDT = D / 32, TILE = 64 * 2 * D;
@@ -1704,16 +1704,15 @@ __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   auto iteration = [&](auto pc, int j) {
     constexpr int P = decltype(pc)::value & 1;    // slot of tile j
-    // this wave's loads of tile j and the lookup of tile j+1 have landed;
-    // after the barrier so have every wave's, and no wave reads tile j-1,
-    // whose slot tile j+1's loads overwrite.  With STAGED, loads stop at the
-    // last tile, so that the epilogue finds the other slot empty; without,
-    // they run on, zero-filled (measured 1 % faster in mixed launches)
+    // this wave's loads of tile j have landed; after the barrier so have
+    // every wave's, and no wave reads tile j-1, whose slot tile j+1's loads
+    // overwrite.  Loads stop at the last tile, so that the epilogue finds the
+    // other slot empty.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     asm volatile("s_barrier" ::: "memory");
-    if (!STAGED || j + 2 < nt) e_next = fetch(j + 2);
+    if (j + 2 < nt) e_next = fetch(j + 2);
     __builtin_amdgcn_sched_barrier(0);
-    if (!STAGED || j + 1 < nt) load_tile(j + 1, kreg + TILE * (P ^ 1), vreg + TILE * (P ^ 1), e_cur);
+    if (j + 1 < nt) load_tile(j + 1, kreg + TILE * (P ^ 1), vreg + TILE * (P ^ 1), e_cur);
     e_cur = e_next;
     const int j0 = kv0 + 64 * j;
     if (j >= 0 && wave_rows && j0 <= wave_last)
@@ -1735,7 +1734,7 @@ __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t
   const bool empty = !(ll > 0.f);
   const float inv = empty ? 0.f : fo / lr;
   const float lse_v = empty ? kNegInf : (mr + __log2f(ll)) * kLn2;
-  if (STAGED && it.prow < 0) {
+  if (it.prow < 0) {
     // the slot of tile nt holds nothing and no load is in flight (loads stop
     // at the last tile, and after the last barrier no wave reads it): 32 KB,
     // 8 KB per wave
@@ -1743,20 +1742,6 @@ __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t
     store_rows_staged<NDT>(o, inv, region, lane, a.out, a.H, t0, it.row0 + wave * 32,
                            nrows - wave * 32, G, it.kvh);
     if (h == 0 && a.lse && row_ok) a.lse[(int64_t)(t0 + tok) * a.H + head] = lse_v;
-  } else if (it.prow < 0) {
-    if (!row_ok) return;
-    const int64_t orow = (int64_t)(t0 + tok) * a.H + head;
-    uint16_t* op = a.out + orow * D + 4 * h;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int ig = 0; ig < 4; ++ig) {
-        uint2 w;
-        w.x = pack_bf16x2(o[dt][4 * ig] * inv, o[dt][4 * ig + 1] * inv);
-        w.y = pack_bf16x2(o[dt][4 * ig + 2] * inv, o[dt][4 * ig + 3] * inv);
-        *reinterpret_cast<uint2*>(op + 32 * dt + 8 * ig) = w;
-      }
-    if (h == 0 && a.lse) a.lse[orow] = lse_v;
   } else {
     if (!row_ok) return;
     float* pp = a.part_o + (int64_t)(it.prow + rl) * D + 4 * h;
@@ -1782,7 +1767,7 @@ __global__ __launch_bounds__(256, 2) void attn_tiled_dma4_kernel(AttnArgs a) {
   constexpr int TILE = 64 * 2 * D;
   __shared__ __attribute__((aligned(1024))) uint8_t lds_a[2 * TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_b[2 * TILE];
-  tiled_dma4_body<D, true>(a, a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS, lds_a, lds_b);
+  tiled_dma4_body<D>(a, a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS, lds_a, lds_b);
 }
 
 // Mixed launch of a bf16 cache at D = 128 with a power-of-two block size:
@@ -1796,9 +1781,7 @@ __global__ __launch_bounds__(256, 2) void attn_mixed_dma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_b[2 * TILE];
   const int32_t* item = a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS;
   if (ld_uniform(item + 7))
-    // (loads through the last tile pair and outputs stored directly: the
-    // staged form measured 1 % slower here)
-    tiled_dma4_body<D, false>(a, item, lds_a, lds_b);
+    tiled_dma4_body<D>(a, item, lds_a, lds_b);
   else
     small_body<D, false, SmallCfg<D>::PF>(a, item, lds_a);
 }
