@@ -340,7 +340,7 @@ def kernel_names(res, fp8):
     elif p["num_small_items"]:
         k = ["attn_small_kernel" + tag]
     elif p["tiled_rows"] == 256:
-        k = ["attn_tiled_dma_kernel<128>" if dma else "attn_tiled_wide_kernel" + tag]
+        k = ["attn_tiled_wide_kernel" + tag]
     else:
         k = ["attn_tiled_dma4_kernel<128>" if dma else "attn_tiled_kernel" + tag]
     if p["num_reduce_items"]:

@@ -11,14 +11,13 @@
 //                              bound by the matrix cores
 //   attn_tiled_wide_kernel<D>  the same for 256-row blocks: 8 waves share
 //                              each K/V tile (long prefills, D <= 128)
-//   attn_tiled_dma_kernel<128> 256-row blocks of a bf16 cache with a
-//                              power-of-two block size: K/V tiles go from
-//                              HBM to LDS by DMA, two tiles ahead
 //   attn_mixed_kernel<D>       small-row and 128-row items in one launch
 //   attn_mixed_dma_kernel<128> the same for a bf16 cache with a power-of-two
 //                              block size, its 128-row items loading K/V
 //                              tiles into LDS by DMA (tiled_dma4_body)
 //   attn_tiled_dma4_kernel<128> 128-row items alone, by tiled_dma4_body
+//                              (every tiled-only launch of a bf16 cache at
+//                              D = 128 with a power-of-two block size)
 //   split_reduce_kernel<D>     LSE merge of split-KV partials (section 1.3
 //                              num_splits)
 //   merge_states_kernel        two-way LSE merge (section 6.3, step 3)
@@ -1165,26 +1164,25 @@ __global__ __launch_bounds__(512, 2) void attn_tiled_wide_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 256-row tiled attention with LDS-DMA tile loads (bf16 cache, D = 128,
-// block size a power of two >= 16): 8 waves of 32 rows share each 64-key
-// K/V tile, one workgroup per compute unit.  Tiles go from HBM straight to
-// LDS (buffer_load_dwordx4 ... lds), two tiles ahead, into a ring of three
-// slots per plane (96 KB): no register holds a tile in flight and no LDS
-// store runs, so a wave's work per tile is its QK^T, softmax and PV alone.
-//   * Each wave issues 2 loads per plane and tile: instruction i (0..15)
-//     fills LDS bytes 1024 i .. 1024 i + 1023 with 8 key rows x 8 chunks of
-//     16 bytes (8 whole 128-byte lines of the cache).  Lane l writes the 16
-//     bytes at 16 l; which chunk a lane fetches sets the layout, chosen so
-//     that the operand reads hit all 64 banks once and their addresses are
-//     one register plus constants.
+// LDS-DMA tile loads (bf16 cache, D = 128, block size a power of two >= 16).
+// K/V tiles go from HBM straight to LDS (buffer_load_dwordx4 ... lds): no
+// register holds a tile in flight and no LDS store runs.
+//   * A 64-key tile of one plane is 16 loads: load i (0..15) fills LDS bytes
+//     1024 i .. 1024 i + 1023 with 8 key rows x 8 chunks of 16 bytes (8 whole
+//     128-byte lines of the cache).  Lane l writes the 16 bytes at 16 l;
+//     which chunk a lane fetches sets the layout, chosen so that the operand
+//     reads hit all 64 banks once and their addresses are one register plus
+//     constants:
+//       K: unit 8 p + r8 holds row r8, chunk 8 ch + (p ^ (rg & 1))
+//       V: unit 8 r8 + p holds row r8, chunk 8 ch + (p ^ 4 ((r8 >> 1) & 1))
+//     (rg = i / 2, ch = i % 2).
 //   * A 16-key group lies in one cache block (tiles start on a multiple of
 //     16 keys), so one buffer resource per group covers it; keys past the
 //     range and entries outside [0, NB) read as zeros.
-//   * Block-table entries are vector loads one tile before their tile's
-//     loads, so their waits count in order with the tiles' loads.
-//   * Each slot is an array of its own, named statically by a loop unrolled
-//     by three: the compiler makes an LDS read wait only for LDS-DMA loads
-//     into the array it reads.
+//   * Block-table entries are scalar loads one tile ahead.
+//   * The LDS address of each load passes through readfirstlane, so the
+//     compiler ties no load to an LDS array and adds no wait of its own: the
+//     explicit waits and barriers of the tile loop order loads and reads.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 template <int N>
@@ -1241,283 +1239,12 @@ __device__ __forceinline__ void store_rows_staged(const f32x16_t* o, float inv, 
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(512, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_tiled_dma_kernel(AttnArgs a) {
-  static_assert(D == 128, "LDS-DMA tiled kernel");
-  constexpr int NKT = D / 16, NDT = D / 32, TILE = 64 * 2 * D;
-  __shared__ __attribute__((aligned(1024))) uint8_t ks0[TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t ks1[TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t ks2[TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs0[TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs1[TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs2[TILE];
-  auto kslot = [&](auto pc) -> uint8_t* {
-    constexpr int s = decltype(pc)::value % 3;
-    if constexpr (s == 0) return ks0;
-    else if constexpr (s == 1) return ks1;
-    else return ks2;
-  };
-  auto vslot = [&](auto pc) -> uint8_t* {
-    constexpr int s = decltype(pc)::value % 3;
-    if constexpr (s == 0) return vs0;
-    else if constexpr (s == 1) return vs1;
-    else return vs2;
-  };
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 31, h = lane >> 5;
-  const Item it = load_item(a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS);
-  const int t0 = it.t0, G = a.G, nrows = it.nrows, kv0 = it.kv0;
-  const int kv1 = min(it.kv1, a.MB * a.BS);
-  const int nt = kv1 > kv0 ? (kv1 - kv0 + 63) >> 6 : 0;
-  const float sl2 = a.scale_log2;
-
-  const int rl = wave * 32 + n;
-  const int r = it.row0 + rl;
-  const bool row_ok = rl < nrows;
-  const int tok = r / G;
-  const int head = it.kvh * G + (r - tok * G);
-  const int row_limit = a.causal ? tok + it.koff : INT_MAX;
-  const int row_lo = a.window > 0 ? tok + it.koff - (a.window - 1) : INT_MIN;
-  const int wave_limit = a.causal ? (it.row0 + wave * 32) / G + it.koff : INT_MAX;
-  const int wave_lo = a.window > 0 ? (it.row0 + wave * 32 + 31) / G + it.koff - (a.window - 1) : INT_MIN;
-  const bool wave_rows = wave * 32 < nrows;
-  const int wave_last = a.causal ? (it.row0 + min(wave * 32 + 31, nrows - 1)) / G + it.koff : INT_MAX;
-
-  bf16x8_t qf[NKT];
-  if (row_ok) {
-    const uint16_t* qp = a.q + ((int64_t)(t0 + tok) * a.H + head) * D + 8 * h;
-#pragma unroll
-    for (int t = 0; t < NKT; ++t) qf[t] = ld16(qp + 16 * t);
-  } else {
-#pragma unroll
-    for (int t = 0; t < NKT; ++t) qf[t] = zero8();
-  }
-
-  // ---- loader.  Instruction i (0..15) of a plane fills LDS bytes
-  // 1024 i .. 1024 i + 1023 with the 8 key rows 8 rg .. 8 rg + 7 (rg = i / 2)
-  // and the 8 chunks 8 ch .. 8 ch + 7 (ch = i % 2) of each: 8 full 128-byte
-  // lines.  Lane l writes 16 bytes at 16 l; which chunk it fetches sets the
-  // layout:
-  //   K: unit 8 p + r8 holds row r8, chunk 8 ch + (p ^ (rg & 1))   (chunk-major)
-  //   V: unit 8 r8 + p holds row r8, chunk 8 ch + (p ^ 4 ((r8 >> 1) & 1))
-  // Wave w issues i = w and i = w + 8: 16-key groups w / 4 and w / 4 + 2, and
-  // the same row within the group (8 ((w / 2) & 1) + r8) and chunk for both.
-  const int64_t row_elems = (int64_t)a.Hkv * D;
-  const int row_bytes = (int)(row_elems * 2);
-  const int rgo = (wave >> 1) & 1, chh = wave & 1;
-  const int voff_k = (8 * rgo + (lane & 7)) * row_bytes + ((8 * chh + ((lane >> 3) ^ rgo)) << 4);
-  const int vr8 = lane >> 3;
-  const int voff_v = (8 * rgo + vr8) * row_bytes + ((8 * chh + ((lane & 7) ^ (4 * ((vr8 >> 1) & 1)))) << 4);
-  const uint8_t* cache_b = reinterpret_cast<const uint8_t*>(a.cache) + (int64_t)it.kvh * D * 2;
-  const int32_t* btrow = a.block_table + (int64_t)it.seq * a.bt_stride;
-  const int bs_log2 = a.bs_log2;
-  const int last_blk = kv1 > 0 ? (kv1 - 1) >> bs_log2 : 0;
-  const int64_t blk_bytes = (int64_t)row_bytes << bs_log2;
-  const int64_t plane_bytes = a.plane * 2;
-  const int grp0 = wave >> 2;              // the wave's two groups: grp0 and grp0 + 2
-  // block-table entries of tile t's four 16-key groups (clamped to the
-  // range's last block)
-  auto fetch = [&](int t) -> TileEntries {
-    const int k0 = kv0 + 64 * t;
-    return TileEntries{ld_uniform(btrow + min(k0 >> bs_log2, last_blk)),
-                       ld_uniform(btrow + min((k0 + 16) >> bs_log2, last_blk)),
-                       ld_uniform(btrow + min((k0 + 32) >> bs_log2, last_blk)),
-                       ld_uniform(btrow + min((k0 + 48) >> bs_log2, last_blk))};
-  };
-  // the LDS address passes through readfirstlane, so that the compiler ties
-  // no load to an LDS array and adds no wait of its own (the waits and
-  // barriers of the loop order the loads and the reads)
-  auto dma = [&](__amdgpu_buffer_rsrc_t rs, uint8_t* dst, int voff) {
-    const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_ptr)dst);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)(uintptr_t)la, 16, voff, 0, 0, 0);
-  };
-  auto load_tile = [&](int t, uint8_t* kd, uint8_t* vd, const TileEntries& ent) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int grp = grp0 + 2 * q;
-      const int g = wave + 8 * q;
-      const int phys = ent.get(grp);
-      const int key0 = kv0 + 64 * t + 16 * grp;
-      const bool ok = (key0 < kv1) & ((unsigned)phys < (unsigned)a.NB);
-      const int64_t x = (int64_t)phys * blk_bytes + (int64_t)(key0 & (a.BS - 1)) * row_bytes;
-      const int64_t boff = x & -(int64_t)ok;
-      const int nrec = ((min(16, kv1 - key0) - 1) * row_bytes + D * 2) & -(int)ok;
-      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint8_t*>(cache_b + boff), 0, nrec, 0x00020000);
-      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint8_t*>(cache_b + plane_bytes + boff), 0, nrec, 0x00020000);
-      dma(rk, kd + 1024 * g, voff_k);
-      dma(rv, vd + 1024 * g, voff_v);
-    }
-  };
-  constexpr int kLoadsPerTile = 4;
-
-  // ---- read addresses.  K operand of k-step t, key half u (row r = n + 32u,
-  // chunk C = 2t + h): 2048 (r / 8) + 1024 (C / 8) + 128 ((C % 8) ^ ((r / 8) & 1))
-  // + 16 (r % 8) = kbase + 8192 u + 1024 (t / 4) + 256 (t % 4).  V operand of d
-  // tile dt, 16-key step ks, second half e (row 16 ks + 8 e + r8, local chunk
-  // cl of the tile's 4): vbase(dt % 2) + 4096 ks + 2048 e + 1024 (dt / 2).
-  // Both are conflict-free: the 16 lanes of a K read and the 32 lanes of a
-  // transposing read cover all 64 banks once.
-  const int n8 = n >> 3;
-  const int kbase = 2048 * n8 + 128 * (h ^ (n8 & 1)) + 16 * (n & 7);
-  const int q16 = lane >> 4, s16 = lane & 15;
-  const int r8v = 4 * h + (s16 >> 2);
-  const int clv = 2 * (q16 & 1) + ((s16 & 3) >> 1);
-  const int vbase0 = 128 * r8v + 16 * clv + 8 * (s16 & 1) + 64 * ((r8v >> 1) & 1);
-  const int vbase1 = vbase0 ^ 64;
-
-  float m_run = kNegInf, l_run = 0.f, lr_run = 0.f;
-  f32x16_t o[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-
-  // (forced inline: three unrolled calls exceed the inliner's budget, and an
-  // outlined tile would keep O and the row state in scratch memory)
-  auto tile = [&](int j0, const uint8_t* kb, const uint8_t* vb, bool masked) __attribute__((always_inline)) {
-    f32x16_t s[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[u][i] = 0.f;
-#pragma unroll
-    for (int t = 0; t < NKT; ++t)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kb + kbase + 8192 * u + 1024 * (t >> 2) + 256 * (t & 3));
-        s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[t], s[u], 0, 0, 0);
-      }
-    float x[32];
-    const int lim = min(kv1 - 1, row_limit) - j0 - 4 * h;
-    const int lim_lo = (row_lo == INT_MIN) ? INT_MIN : row_lo - j0 - 4 * h;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) x[16 * u + i] = s[u][i];
-    if (masked) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int off = 32 * (i >> 4) + 8 * ((i & 15) >> 2) + (i & 3);
-        x[i] = (off > lim || off < lim_lo) ? kNegInf : x[i];
-      }
-    }
-    float mx = x[0];
-#pragma unroll
-    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, x[i]);
-    mx = max_xor<32>(mx) * sl2;
-    if (__builtin_expect(__any(mx > m_run + kRescaleSlack), 0)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-      lr_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-      m_run = m_new;
-    }
-    const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], sl2, neg_m));
-      ps[i & 3] += x[i];
-    }
-    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    bf16x8_t pb[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      pb[ks] = pack_bf16x8(x + 8 * ks);
-      lr_run = add_bf16x8(pb[ks], lr_run);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const uint8_t* p0 = vb + ((dt & 1) ? vbase1 : vbase0) + 4096 * ks + 1024 * (dt >> 1);
-        const bf16x8_t av = cat(lds_read_tr(reinterpret_cast<const uint16_t*>(p0)),
-                                lds_read_tr(reinterpret_cast<const uint16_t*>(p0 + 2048)));
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks], o[dt], 0, 0, 0);
-      }
-    }
-  };
-
-  // ---- the loop starts two tiles early (j = -2, -1 only issue loads), so
-  // that the first tiles load as the later ones do; loads and lookups stop at
-  // the last tile.  The lookup of tile 0 and the Q loads land before the loop.
-  TileEntries e_cur = nt > 0 ? fetch(0) : TileEntries{0, 0, 0, 0};   // entries of tile j+2 at the top of iteration j
-  TileEntries e_next = e_cur;
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  auto iteration = [&](auto pc, int j) {
-    constexpr int P = decltype(pc)::value;    // slot of tile j (j mod 3)
-    // tile j has landed (only tile j+1's loads may be in flight, and none
-    // past the last tile); after the barrier every wave is done with tile
-    // j-1, whose slots tile j+2's loads overwrite
-    if (j + 1 < nt)
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoadsPerTile));
-    else
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    // a workgroup barrier with no memory fence: a fence would wait for every
-    // LDS-DMA load in flight, tile j+1's too ("memory" keeps the compiler
-    // from moving LDS accesses across it)
-    asm volatile("s_barrier" ::: "memory");
-    if (j + 3 < nt) e_next = fetch(j + 3);
-    __builtin_amdgcn_sched_barrier(0);
-    if (j + 2 < nt) load_tile(j + 2, kslot(IntC<P + 2>{}), vslot(IntC<P + 2>{}), e_cur);
-    e_cur = e_next;
-    const int j0 = kv0 + 64 * j;
-    if (j >= 0 && wave_rows && j0 <= wave_last)
-      tile(j0, kslot(pc), vslot(pc), j0 + 64 > kv1 || j0 + 63 > wave_limit || j0 < wave_lo);
-  };
-  for (int j = nt > 0 ? -2 : 0;;) {
-    if (j >= nt) break;
-    iteration(IntC<1>{}, j++);
-    if (j >= nt) break;
-    iteration(IntC<2>{}, j++);
-    if (j >= nt) break;
-    iteration(IntC<0>{}, j++);
-  }
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-
-  // ---- epilogue (as attn_tiled_kernel; whole outputs go through LDS)
-  const float l = sum_xor<32>(l_run);
-  float lr = sum_xor<32>(lr_run);
-  float mr = m_run, ll = l, fo = 1.f;
-  if (a.s_aux && it.prow < 0 && row_ok) fo = add_sink(a.s_aux[head] * kLog2e, mr, ll, lr);
-  const bool empty = !(ll > 0.f);
-  const float inv = empty ? 0.f : fo / lr;
-  const float lse_v = empty ? kNegInf : (mr + __log2f(ll)) * kLn2;
-  if (it.prow < 0) {
-    // the slots of tiles nt and nt+1 hold nothing and no load is in flight
-    // (loads stop at the last tile, and after the last barrier no wave reads
-    // them): 64 KB, 8 KB per wave
-    const int s = (nt + ((wave >> 1) & 1)) % 3;
-    uint8_t* region = wave < 4 ? (s == 0 ? ks0 : s == 1 ? ks1 : ks2) : (s == 0 ? vs0 : s == 1 ? vs1 : vs2);
-    store_rows_staged<NDT>(o, inv, region + 8192 * (wave & 1), lane, a.out, a.H, t0,
-                           it.row0 + wave * 32, nrows - wave * 32, G, it.kvh);
-    if (h == 0 && a.lse && row_ok) a.lse[(int64_t)(t0 + tok) * a.H + head] = lse_v;
-  } else {
-    if (!row_ok) return;
-    float* pp = a.part_o + (int64_t)(it.prow + rl) * D + 4 * h;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int ig = 0; ig < 4; ++ig)
-        *reinterpret_cast<f32x4_t*>(pp + 32 * dt + 8 * ig) =
-            f32x4_t{o[dt][4 * ig] * inv, o[dt][4 * ig + 1] * inv, o[dt][4 * ig + 2] * inv,
-                    o[dt][4 * ig + 3] * inv};
-    if (h == 0) a.part_lse[it.prow + rl] = lse_v;
-  }
-}
 
 // ---------------------------------------------------------------------------
-// 4-wave LDS-DMA tiled body (128-row items of a mixed launch, bf16 cache,
-// D = 128, block size a power of two >= 16): the tile loads and layouts of
-// attn_tiled_dma_kernel, double-buffered (tile j+1 loads while tile j is
-// computed) in 64 KB, so that two workgroups still fit a compute unit beside
-// the small-row items of the same launch.
+// 4-wave LDS-DMA tiled body (128-row items, bf16 cache, D = 128, block size a
+// power of two >= 16): the DMA tile loads above, double-buffered (tile j+1
+// loads while tile j is computed) in 64 KB, so that two workgroups fit a
+// compute unit, beside each other or beside small-row items.
 // ---------------------------------------------------------------------------
 template <int D>
 __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t* item, uint8_t* kreg, uint8_t* vreg) {
@@ -1554,9 +1281,9 @@ __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t
     for (int t = 0; t < NKT; ++t) qf[t] = zero8();
   }
 
-  // ---- loader: the loads and LDS layouts of attn_tiled_dma_kernel; wave w
-  // (0..3) issues i = w, w + 4, w + 8, w + 12 (16-key groups 0..3), with the
-  // same row within the group (8 ((w / 2) & 1) + r8) and chunk for all four
+  // ---- loader (the DMA loads and layouts above): wave w (0..3) issues
+  // i = w, w + 4, w + 8, w + 12 (16-key groups 0..3), with the same row
+  // within the group (8 ((w / 2) & 1) + r8) and chunk for all four
   const int64_t row_elems = (int64_t)a.Hkv * D;
   const int row_bytes = (int)(row_elems * 2);
   const int rgo = (wave >> 1) & 1, chh = wave & 1;
@@ -1759,9 +1486,8 @@ __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t
 // 128-row tiled items alone (bf16 cache, D = 128, power-of-two block size):
 // two 4-wave workgroups per compute unit, each double-buffering its tiles,
 // so that one workgroup's first loads and last stores overlap the other's
-// tiles.  Measured on the mix's 8 prefills (592-1811 tokens): 141-144 us
-// against 146-147 us for 256-row blocks in attn_tiled_dma_kernel; on 4 x 8192
-// tokens 2435-2464 us against 2395-2402 us, so long prefills keep 256 rows.
+// tiles.  It measured faster than an 8-wave form with 256-row items sharing
+// each tile, at every length tried (592-1811 and 8192 tokens).
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_tiled_dma4_kernel(AttnArgs a) {
   constexpr int TILE = 64 * 2 * D;
@@ -1963,18 +1689,9 @@ pa_status launch_fwd(const AttnArgs& base, const pa_plan_info* plan, const int32
     bool launched = false;
     if constexpr (D <= 128) {
       if (plan->tiled_rows == PA_TILED_ROWS_WIDE) {
-        if constexpr (D == 128 && !FP8) {
-          if (a.bs_log2 >= 4) {
-            hipLaunchKernelGGL((attn_tiled_dma_kernel<D>), dim3(plan->num_tiled_items),
-                               dim3(512), 0, stream, a);
-            launched = true;
-          }
-        }
-        if (!launched) {
-          hipLaunchKernelGGL((attn_tiled_wide_kernel<D, FP8>), dim3(plan->num_tiled_items),
-                             dim3(512), 0, stream, a);
-          launched = true;
-        }
+        hipLaunchKernelGGL((attn_tiled_wide_kernel<D, FP8>), dim3(plan->num_tiled_items),
+                           dim3(512), 0, stream, a);
+        launched = true;
       }
     }
     if constexpr (D == 128 && !FP8) {

@@ -270,13 +270,15 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
   thread_local std::vector<Unit> units;
   units.clear();
   // Tiled row blocks: PA_TILED_ROWS_WIDE rows (8-wave workgroups sharing each
-  // K/V tile) when no sequence is small-row, D <= 128, and the prefills are
-  // long (2048 query tokens or more on average) or D = 64; else PA_TILED_ROWS
-  // (4-wave workgroups, which a mixed launch shares with small-row items).
-  // Measured on MI355X (H = 32, Hkv = 8, causal): 256-row blocks took 4-9 %
-  // less time for prefills of 2048-8192 tokens and 3 % less at D = 64 for
-  // 256-2048 tokens, but 2-3 % more at D = 128 for 592-1811 tokens (with DMA
-  // tile loads in both kernels, as with register-staged loads).
+  // K/V tile) when no sequence is small-row, D <= 128, and either D = 64 or
+  // the prefills are long (2048 query tokens or more on average) and the
+  // cache is not one that the DMA kernel runs (bf16 at D = 128 with a
+  // power-of-two block size); else PA_TILED_ROWS (4-wave workgroups).
+  // Measured on MI355X (H = 32, Hkv = 8, causal): with register-staged tile
+  // loads 256-row blocks took 4-9 % less time for prefills of 2048-8192
+  // tokens and 3 % less at D = 64 for 256-2048 tokens; with DMA tile loads
+  // 128-row blocks in two workgroups per compute unit were faster at every
+  // length (3 % on 4 x 8192 tokens, 4-8 % on 592-1811 tokens).
   bool any_small = false;
   int64_t tiled_q = 0, tiled_seqs = 0;
   for (int32_t b = 0; b < B; ++b) {
@@ -289,8 +291,10 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
       ++tiled_seqs;
     }
   }
+  const bool dma_kernel = p->head_size == 128 && !p->kv_cache_fp8 &&
+                          (p->block_size & (p->block_size - 1)) == 0;
   const bool wide = !any_small && tiled_seqs > 0 && p->head_size <= 128 &&
-                    (p->head_size <= 64 || tiled_q >= 2048 * tiled_seqs);
+                    (p->head_size <= 64 || (tiled_q >= 2048 * tiled_seqs && !dma_kernel));
   const int32_t tiled_rows = wide ? PA_TILED_ROWS_WIDE : PA_TILED_ROWS;
   for (int32_t b = 0; b < B; ++b) {
     const int32_t Lq = cu[b + 1] - cu[b], Lk = sk[b];

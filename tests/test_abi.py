@@ -615,10 +615,11 @@ def test_num_cus(L):
 
 
 def test_wide_rows_rule(L):
-    """Prefill-only plans use 256-row blocks at D = 64 or when the prefills
-    average 2048 query tokens or more, whatever the block size or cache
-    format; the 8 prefills of chunked_prefill_mix (592-1811 tokens) keep
-    128-row blocks, and a plan with decode rows always does."""
+    """Prefill-only plans use 256-row blocks at D = 64, or when the prefills
+    average 2048 query tokens or more and the cache is one the DMA kernel
+    does not run (E4M3, or a block size that is not a power of two); the 8
+    prefills of chunked_prefill_mix (592-1811 tokens) keep 128-row blocks
+    either way, and a plan with decode rows always does."""
     def rows(name, bs=None, fp8=False, d=None):
         wl = W.make(name, materialise=False)
         bs = bs or wl.BS
@@ -629,7 +630,10 @@ def test_wide_rows_rule(L):
     short, long_ = "chunked_prefill_mix_prefill", "prefill_causal_8k"
     for kw in ({}, {"bs": 64}, {"bs": 48}, {"fp8": True}):
         assert rows(short, **kw) == ops.PA_TILED_ROWS
-        assert rows(long_, **kw) == ops.PA_TILED_ROWS_WIDE
+    assert rows(long_) == ops.PA_TILED_ROWS                   # bf16, BS = 32: DMA kernel
+    assert rows(long_, bs=64) == ops.PA_TILED_ROWS
+    assert rows(long_, bs=48) == ops.PA_TILED_ROWS_WIDE
+    assert rows(long_, fp8=True) == ops.PA_TILED_ROWS_WIDE
     assert rows(short, d=64) == ops.PA_TILED_ROWS_WIDE
     assert rows("chunked_prefill_mix") == ops.PA_TILED_ROWS
 

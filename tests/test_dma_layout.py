@@ -1,5 +1,5 @@
-"""The LDS layouts of attn_tiled_dma_kernel<128> and tiled_dma4_body
-(paged_kv_varlen_flash_amd/csrc/pagedattn.hip), modelled on the CPU: the index formulas of its loader
+"""The LDS layouts of the DMA tile loads (tiled_dma4_body in
+paged_kv_varlen_flash_amd/csrc/pagedattn.hip), modelled on the CPU: the index formulas of its loader
 and of its operand reads, restated here, must put every (key row, 16-byte
 chunk) of a 64-key tile in LDS exactly once, give each MFMA operand read the
 elements that the row-major layout of attn_tiled_kernel gives it, and hit
@@ -11,10 +11,11 @@ ROW_BYTES_CASES = (256, 1024, 4096)   # Hkv * D * 2 for Hkv = 1, 4, 16
 
 
 def loader(row_bytes, waves=8):
-    """{LDS byte offset: (row, chunk)} of the K and V planes.  8 waves
-    (attn_tiled_dma_kernel): wave w issues loads i = w and w + 8 of each plane;
-    4 waves (tiled_dma4_body): i = w, w + 4, w + 8, w + 12.  Lane l writes 16
-    bytes at 1024 i + 16 l with the chunk its voffset selects."""
+    """{LDS byte offset: (row, chunk)} of the K and V planes.  4 waves
+    (tiled_dma4_body): wave w issues loads i = w, w + 4, w + 8, w + 12 of each
+    plane; 8 waves (the same loads shared by two more waves, as an 8-wave form
+    would issue them): i = w and w + 8.  Lane l writes 16 bytes at
+    1024 i + 16 l with the chunk its voffset selects."""
     K, V = {}, {}
     for w in range(waves):
         rgo, chh = (w >> 1) & 1, w & 1

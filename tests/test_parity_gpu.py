@@ -220,8 +220,9 @@ def test_prefill_only(case):
         f"force={force}")
     plan = _check_case(spec, np.random.default_rng(7000 + case), force, f"prefill_only{case}")
     assert plan.info.num_small_items == 0 and plan.info.num_tiled_items > 0
-    # 256-row blocks (8-wave workgroups) at D = 64, or for long prefills at D = 128
-    wide = D <= 64 or (D <= 128 and np.mean([q for q, _ in seqs]) >= 2048)
+    # 256-row blocks (8-wave workgroups) at D = 64, or for long prefills at
+    # D = 128 unless the DMA kernel runs them (power-of-two block size)
+    wide = D <= 64 or (D <= 128 and np.mean([q for q, _ in seqs]) >= 2048 and BS & (BS - 1) != 0)
     assert plan.info.tiled_rows == (256 if wide else 128)
 
 

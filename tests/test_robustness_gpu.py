@@ -63,7 +63,8 @@ BAD_ENTRY = [
     (64, 8, 1, 16, True, ((1, 200), (40, 170)), "bf16"),               # D = 64 tiled loader
     (256, 2, 2, 64, True, ((1, 500), (20, 300)), "bf16"),
     (128, 4, 2, 32, True, ((1, 300), (60, 260)), "e4m3"),              # E4M3 loaders
-    (128, 4, 1, 32, True, ((2100, 2300), (2050, 2050)), "bf16"),       # 256-row DMA loads
+    (128, 4, 1, 32, True, ((2100, 2300), (2050, 2050)), "bf16"),       # DMA loads, no decode rows
+    (128, 4, 1, 48, True, ((2100, 2300), (2050, 2050)), "bf16"),       # 256-row blocks (BS = 48)
 ]
 
 
