@@ -1167,9 +1167,9 @@ __global__ __launch_bounds__(512, 2) void attn_tiled_wide_kernel(AttnArgs a) {
 // LDS-DMA tile loads (bf16 cache, D = 128, block size a power of two >= 16).
 // K/V tiles go from HBM straight to LDS (buffer_load_dwordx4 ... lds): no
 // register holds a tile in flight and no LDS store runs.
-//   * A 64-key tile of one plane is 16 loads: load i (0..15) fills LDS bytes
-//     1024 i .. 1024 i + 1023 with 8 key rows x 8 chunks of 16 bytes (8 whole
-//     128-byte lines of the cache).  Lane l writes the 16 bytes at 16 l;
+//   * A tile of kDmaTileKeys keys of one plane is kDmaTileKeys / 4 loads:
+//     load i fills LDS bytes 1024 i .. 1024 i + 1023 with 8 key rows x 8
+//     chunks of 16 bytes (8 whole 128-byte lines of the cache).  Lane l writes the 16 bytes at 16 l;
 //     which chunk a lane fetches sets the layout, chosen so that the operand
 //     reads hit all 64 banks once and their addresses are one register plus
 //     constants:
@@ -1185,6 +1185,10 @@ __global__ __launch_bounds__(512, 2) void attn_tiled_wide_kernel(AttnArgs a) {
 //     explicit waits and barriers of the tile loop order loads and reads.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
+// keys per tile: 32-key tiles keep a workgroup at 32 KB of LDS and 160 VGPRs,
+// so that three fit a compute unit (measured faster than 64-key tiles at two
+// workgroups per compute unit on every prefill length tried)
+constexpr int kDmaTileKeys = 32;
 template <int N>
 struct IntC {
   static constexpr int value = N;
@@ -1192,13 +1196,13 @@ struct IntC {
 // s_waitcnt with only the vector-memory count bounded (gfx9 encoding)
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-// Block-table entries of one 64-key tile's four 16-key groups, read by
-// scalar loads: their waits count on lgkmcnt, which nothing else holds at
-// the top of a tile iteration (the previous tile's LDS reads have all been
+// Block-table entries of one tile's two 16-key groups, read by scalar
+// loads: their waits count on lgkmcnt, which nothing else holds at the top
+// of a tile iteration (the previous tile's LDS reads have all been
 // consumed), so waiting for them never waits for a tile load in flight.
 struct TileEntries {
-  int e0, e1, e2, e3;
-  __device__ int get(int g) const { return g == 0 ? e0 : g == 1 ? e1 : g == 2 ? e2 : e3; }
+  int e0, e1;
+  __device__ int get(int g) const { return g == 0 ? e0 : e1; }
 };
 
 // Stores one wave's 32 rows of O (lane (n, h) holds, in o[dt][4 ig + e],
@@ -1243,20 +1247,22 @@ __device__ __forceinline__ void store_rows_staged(const f32x16_t* o, float inv, 
 // ---------------------------------------------------------------------------
 // 4-wave LDS-DMA tiled body (128-row items, bf16 cache, D = 128, block size a
 // power of two >= 16): the DMA tile loads above, double-buffered (tile j+1
-// loads while tile j is computed) in 64 KB, so that two workgroups fit a
+// loads while tile j is computed) in 32 KB, so that three workgroups fit a
 // compute unit, beside each other or beside small-row items.
 // ---------------------------------------------------------------------------
 template <int D>
 __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t* item, uint8_t* kreg, uint8_t* vreg) {
   static_assert(D == 128, "4-wave LDS-DMA tiled body");
-  constexpr int NKT = D / 16, NDT = D / 32, TILE = 64 * 2 * D;
+  // KT keys per tile: NG 16-key groups, NU 32-key halves of the score tile
+  constexpr int KT = kDmaTileKeys, NKT = D / 16, NDT = D / 32, TILE = KT * 2 * D, NG = KT / 16,
+                NU = KT / 32;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
   const Item it = load_item(item);
   const int t0 = it.t0, G = a.G, nrows = it.nrows, kv0 = it.kv0;
   const int kv1 = min(it.kv1, a.MB * a.BS);
-  const int nt = kv1 > kv0 ? (kv1 - kv0 + 63) >> 6 : 0;
+  const int nt = kv1 > kv0 ? (kv1 - kv0 + KT - 1) / KT : 0;
   const float sl2 = a.scale_log2;
 
   const int rl = wave * 32 + n;
@@ -1282,8 +1288,8 @@ __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t
   }
 
   // ---- loader (the DMA loads and layouts above): wave w (0..3) issues
-  // i = w, w + 4, w + 8, w + 12 (16-key groups 0..3), with the same row
-  // within the group (8 ((w / 2) & 1) + r8) and chunk for all four
+  // i = w and w + 4 (16-key groups 0 and 1), with the same row within the
+  // group (8 ((w / 2) & 1) + r8) and chunk for both
   const int64_t row_elems = (int64_t)a.Hkv * D;
   const int row_bytes = (int)(row_elems * 2);
   const int rgo = (wave >> 1) & 1, chh = wave & 1;
@@ -1297,14 +1303,12 @@ __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t
   const int64_t blk_bytes = (int64_t)row_bytes << bs_log2;
   const int64_t plane_bytes = a.plane * 2;
 
-  // block-table entries of tile t's four 16-key groups (clamped to the
+  // block-table entries of tile t's two 16-key groups (clamped to the
   // range's last block)
   auto fetch = [&](int t) -> TileEntries {
-    const int k0 = kv0 + 64 * t;
+    const int k0 = kv0 + KT * t;
     return TileEntries{ld_uniform(btrow + min(k0 >> bs_log2, last_blk)),
-                       ld_uniform(btrow + min((k0 + 16) >> bs_log2, last_blk)),
-                       ld_uniform(btrow + min((k0 + 32) >> bs_log2, last_blk)),
-                       ld_uniform(btrow + min((k0 + 48) >> bs_log2, last_blk))};
+                       ld_uniform(btrow + min((k0 + 16) >> bs_log2, last_blk))};
   };
   // the LDS address passes through readfirstlane, so that the compiler ties
   // no load to an LDS array and adds no wait of its own (the waits and
@@ -1315,11 +1319,11 @@ __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t
   };
   auto load_tile = [&](int t, uint8_t* kd, uint8_t* vd, const TileEntries& ent) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < NG; ++q) {
       const int grp = q;
       const int g = wave + 4 * q;
       const int phys = ent.get(grp);
-      const int key0 = kv0 + 64 * t + 16 * grp;
+      const int key0 = kv0 + KT * t + 16 * grp;
       const bool ok = (key0 < kv1) & ((unsigned)phys < (unsigned)a.NB);
       const int64_t x = (int64_t)phys * blk_bytes + (int64_t)(key0 & (a.BS - 1)) * row_bytes;
       const int64_t boff = x & -(int64_t)ok;
@@ -1358,35 +1362,50 @@ __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t
   // (forced inline: three unrolled calls exceed the inliner's budget, and an
   // outlined tile would keep O and the row state in scratch memory)
   auto tile = [&](int j0, const uint8_t* kb, const uint8_t* vb, bool masked) __attribute__((always_inline)) {
-    f32x16_t s[2];
+    f32x16_t s[NU];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < NU; ++u)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[u][i] = 0.f;
+    constexpr int NR = NU * NKT, AHEAD = NR / 2;
+    bf16x8_t kr[NR];
 #pragma unroll
     for (int t = 0; t < NKT; ++t)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kb + kbase + 8192 * u + 1024 * (t >> 2) + 256 * (t & 3));
-        s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[t], s[u], 0, 0, 0);
-      }
-    float x[32];
+      for (int u = 0; u < NU; ++u)
+        kr[NU * t + u] = *reinterpret_cast<const bf16x8_t*>(kb + kbase + 8192 * u + 1024 * (t >> 2) + 256 * (t & 3));
+#pragma unroll
+    for (int t = 0; t < NKT; ++t)
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+        s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[NU * t + u], qf[t], s[u], 0, 0, 0);
+    // K operand reads run AHEAD of the matrix ops (left to itself the
+    // scheduler kept one read in flight and waited for it before each
+    // product): AHEAD reads, then one product and one read in turn
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);     // DS reads
+#pragma unroll
+    for (int i = 0; i < NR - AHEAD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+    float x[16 * NU];
     const int lim = min(kv1 - 1, row_limit) - j0 - 4 * h;
     const int lim_lo = (row_lo == INT_MIN) ? INT_MIN : row_lo - j0 - 4 * h;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < NU; ++u)
 #pragma unroll
       for (int i = 0; i < 16; ++i) x[16 * u + i] = s[u][i];
     if (masked) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
+      for (int i = 0; i < 16 * NU; ++i) {
         const int off = 32 * (i >> 4) + 8 * ((i & 15) >> 2) + (i & 3);
         x[i] = (off > lim || off < lim_lo) ? kNegInf : x[i];
       }
     }
     float mx = x[0];
 #pragma unroll
-    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, x[i]);
+    for (int i = 1; i < 16 * NU; ++i) mx = fmaxf(mx, x[i]);
     mx = max_xor<32>(mx) * sl2;
     if (__builtin_expect(__any(mx > m_run + kRescaleSlack), 0)) {
       const float m_new = fmaxf(m_run, mx);
@@ -1400,19 +1419,19 @@ __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t
     const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
     float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
+    for (int i = 0; i < 16 * NU; ++i) {
       x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], sl2, neg_m));
       ps[i & 3] += x[i];
     }
     l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    bf16x8_t pb[4];
+    bf16x8_t pb[NG];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < NG; ++ks) {
       pb[ks] = pack_bf16x8(x + 8 * ks);
       lr_run = add_bf16x8(pb[ks], lr_run);
     }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < NG; ++ks) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const uint8_t* p0 = vb + ((dt & 1) ? vbase1 : vbase0) + 4096 * ks + 1024 * (dt >> 1);
@@ -1426,7 +1445,7 @@ __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t
   // ---- double buffer: iteration j issues tile j+1's loads into the other
   // slot after its barrier and computes tile j; the loop starts one tile
   // early (j = -1 only issues loads)
-  TileEntries e_cur = nt > 0 ? fetch(0) : TileEntries{0, 0, 0, 0};   // entries of tile j+1 in iteration j
+  TileEntries e_cur = nt > 0 ? fetch(0) : TileEntries{0, 0};   // entries of tile j+1 in iteration j
   TileEntries e_next = e_cur;
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   auto iteration = [&](auto pc, int j) {
@@ -1441,9 +1460,9 @@ __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t
     __builtin_amdgcn_sched_barrier(0);
     if (j + 1 < nt) load_tile(j + 1, kreg + TILE * (P ^ 1), vreg + TILE * (P ^ 1), e_cur);
     e_cur = e_next;
-    const int j0 = kv0 + 64 * j;
+    const int j0 = kv0 + KT * j;
     if (j >= 0 && wave_rows && j0 <= wave_last)
-      tile(j0, kreg + TILE * P, vreg + TILE * P, j0 + 64 > kv1 || j0 + 63 > wave_limit || j0 < wave_lo);
+      tile(j0, kreg + TILE * P, vreg + TILE * P, j0 + KT > kv1 || j0 + KT - 1 > wave_limit || j0 < wave_lo);
   };
   for (int j = nt > 0 ? -1 : 0;;) {
     if (j >= nt) break;
@@ -1462,10 +1481,11 @@ __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t
   const float inv = empty ? 0.f : fo / lr;
   const float lse_v = empty ? kNegInf : (mr + __log2f(ll)) * kLn2;
   if (it.prow < 0) {
-    // the slot of tile nt holds nothing and no load is in flight (loads stop
-    // at the last tile, and after the last barrier no wave reads it): 32 KB,
-    // 8 KB per wave
-    uint8_t* region = (wave < 2 ? kreg : vreg) + TILE * (nt & 1) + 8192 * (wave & 1);
+    // no load is in flight (loads stop at the last tile), and after this
+    // barrier no wave reads a slot: both slots of both planes, 32 KB, 8 KB
+    // per wave
+    asm volatile("s_barrier" ::: "memory");
+    uint8_t* region = (wave < 2 ? kreg : vreg) + 8192 * (wave & 1);
     store_rows_staged<NDT>(o, inv, region, lane, a.out, a.H, t0, it.row0 + wave * 32,
                            nrows - wave * 32, G, it.kvh);
     if (h == 0 && a.lse && row_ok) a.lse[(int64_t)(t0 + tok) * a.H + head] = lse_v;
@@ -1484,24 +1504,25 @@ __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t
 }
 
 // 128-row tiled items alone (bf16 cache, D = 128, power-of-two block size):
-// two 4-wave workgroups per compute unit, each double-buffering its tiles,
-// so that one workgroup's first loads and last stores overlap the other's
+// three 4-wave workgroups per compute unit, each double-buffering its tiles,
+// so that one workgroup's first loads and last stores overlap the others'
 // tiles.  It measured faster than an 8-wave form with 256-row items sharing
 // each tile, at every length tried (592-1811 and 8192 tokens).
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_tiled_dma4_kernel(AttnArgs a) {
-  constexpr int TILE = 64 * 2 * D;
+  constexpr int TILE = kDmaTileKeys * 2 * D;
   __shared__ __attribute__((aligned(1024))) uint8_t lds_a[2 * TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_b[2 * TILE];
   tiled_dma4_body<D>(a, a.items + (int64_t)blockIdx.x * PA_ITEM_WORDS, lds_a, lds_b);
 }
 
 // Mixed launch of a bf16 cache at D = 128 with a power-of-two block size:
-// small-row items as in attn_mixed_kernel, tiled items by the 4-wave LDS-DMA
-// body.  The small body's staging area and the K slots share lds_a.
+// small-row items as in attn_small_kernel (two load steps in flight), tiled
+// items by the 4-wave LDS-DMA body, three workgroups per compute unit.  The
+// small body's staging area and the K slots share lds_a.
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_mixed_dma_kernel(AttnArgs a) {
-  constexpr int TILE = 64 * 2 * D;
+  constexpr int TILE = kDmaTileKeys * 2 * D;
   constexpr int LA = small_lds_bytes<D>() > 2 * TILE ? small_lds_bytes<D>() : 2 * TILE;
   __shared__ __attribute__((aligned(1024))) uint8_t lds_a[(LA + 1023) / 1024 * 1024];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_b[2 * TILE];
@@ -1509,7 +1530,7 @@ __global__ __launch_bounds__(256, 2) void attn_mixed_dma_kernel(AttnArgs a) {
   if (ld_uniform(item + 7))
     tiled_dma4_body<D>(a, item, lds_a, lds_b);
   else
-    small_body<D, false, SmallCfg<D>::PF>(a, item, lds_a);
+    small_body<D, false, SmallCfg<D>::PF_SMALL>(a, item, lds_a);
 }
 
 // ---------------------------------------------------------------------------

@@ -372,6 +372,8 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
                           (int64_t)(target * (p->head_size >= 256 ? kSmallItemsPerCuD256
                                               : p->kv_cache_fp8 && n_tiled == 0
                                                   ? kSmallItemsPerCuFp8
+                                              : dma_kernel && n_tiled > 0
+                                                  ? kSmallItemsPerCuDmaMix
                                                   : kSmallItemsPerCu))),
                  64) * 64);
     for (const Unit& u : units) {

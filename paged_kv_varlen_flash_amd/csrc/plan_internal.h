@@ -31,6 +31,11 @@ constexpr double kSmallItemsPerCuD256 = 2.5;
 // Used for launches of small items only: with tiled items beside them (a
 // chunked-prefill mix) 3.5 stays faster, 183-185 us against 187-189 us.
 constexpr double kSmallItemsPerCuFp8 = 4.5;
+// mixed launches of the LDS-DMA kernel (bf16 cache, D = 128, power-of-two
+// block size) hold three workgroups per compute unit: 4.5 measured best of
+// 3.5 / 4.5 / 5.5 on the chunked-prefill mix (185.2-186.5 us against
+// 189.1-189.8 us at 3.5; 5.5 within noise of 4.5)
+constexpr double kSmallItemsPerCuDmaMix = 4.5;
 
 static_assert(PA_TILED_ROWS == kTiledWaves * 32, "tiled row block");
 

@@ -392,17 +392,22 @@ def test_fp8_cache_plan(L):
         p = ops.make_params(64, 32, 8, 128, 16, 20000, 256, False, 0.1, kv_cache_fp8=fp8)
         n.append(ops.pa_plan_varlen(p, cu, k_lens)[1].num_small_items)
     assert n[1] > n[0]
-    # beside tiled items (prefill rows) both formats get the same plan
+    # beside tiled items (prefill rows) an E4M3 cache gets the plan of a bf16
+    # cache that the LDS-DMA kernel does not run (block size 48); the DMA
+    # kernel's mixed launch (bf16, power-of-two block size) cuts decode ranges
+    # more finely (three workgroups per compute unit)
     q_mix = np.concatenate([np.ones(56, np.int32), np.full(8, 700, np.int32)])
     k_mix = np.concatenate([k_lens[:56], np.full(8, 900, np.int32)])
     cu_mix = np.concatenate([[0], np.cumsum(q_mix)]).astype(np.int32)
-    words = []
-    for fp8 in (False, True):
-        p = ops.make_params(64, 32, 8, 128, 16, 20000, 256, True, 0.1, kv_cache_fp8=fp8)
+    words, small = [], []
+    for fp8, bs in ((False, 48), (True, 16), (False, 16)):
+        p = ops.make_params(64, 32, 8, 128, bs, 20000, 256, True, 0.1, kv_cache_fp8=fp8)
         w, info = ops.pa_plan_varlen(p, cu_mix, k_mix)
         assert info.num_tiled_items > 0
         words.append(w)
+        small.append(info.num_small_items)
     assert np.array_equal(words[0], words[1])
+    assert small[2] > small[1]
     p = params()
     p.kv_cache_fp8 = 2
     with pytest.raises(ops.PaError) as e:
