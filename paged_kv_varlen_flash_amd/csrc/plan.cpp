@@ -277,8 +277,9 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
   // Measured on MI355X (H = 32, Hkv = 8, causal): with register-staged tile
   // loads 256-row blocks took 4-9 % less time for prefills of 2048-8192
   // tokens and 3 % less at D = 64 for 256-2048 tokens; with DMA tile loads
-  // 128-row blocks in two workgroups per compute unit were faster at every
-  // length (3 % on 4 x 8192 tokens, 4-8 % on 592-1811 tokens).
+  // 128-row blocks in 4-wave workgroups were faster at every length (3 % on
+  // 4 x 8192 tokens, 4-8 % on 592-1811 tokens, measured at two workgroups
+  // per compute unit; they now run three).
   bool any_small = false;
   int64_t tiled_q = 0, tiled_seqs = 0;
   for (int32_t b = 0; b < B; ++b) {

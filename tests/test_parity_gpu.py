@@ -208,6 +208,10 @@ PREFILL_ONLY = [
     (128, 1, 3, 64, True, ((2500, 2400), (1700, 1900)), 0),
     (128, 8, 1, 128, True, ((2049, 4100), (2100, 2100)), 2),
     (128, 4, 2, 48, True, ((2100, 2100), (2050, 2400)), 0),
+    # LDS-DMA tiles (32 keys) inside 256-token blocks, split into forced
+    # pieces whose ends fall inside a tile, and short prefills
+    (128, 4, 2, 256, True, ((333, 333), (45, 1000), (5, 77), (130, 531)), 3),
+    (128, 2, 4, 128, False, ((97, 1201), (300, 300)), 7),
 ]
 
 
