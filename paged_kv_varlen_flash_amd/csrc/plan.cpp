@@ -390,9 +390,20 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
           c = ceil_div32(ceil_div32(kv, nsp), 64) * 64;
         }
       }
+      // a split unit's last piece is cut finer (kSmallTailCuts pieces, 2 in
+      // mixed launches), so that the longest-first order ends on short items
+      // and the launch drains faster (D <= 128)
+      const bool graded = force_splits == 0 && kv > chunk && p->head_size <= 128;
+      const int32_t tail_cuts = n_tiled > 0 ? kSmallTailCutsMixed : kSmallTailCuts;
       int32_t k0 = u.kv_begin;
-      do {
-        const int32_t k1 = std::min(u.kv_end, k0 + std::max(c, 1));
+      int32_t step = std::max(c, 1);
+      do {   // (an empty range still gets its item: its rows are written)
+        int32_t k1 = std::min(u.kv_end, k0 + step);
+        if (graded && k1 == u.kv_end && step == c && k1 - k0 >= 128) {
+          const int32_t q = std::min(tail_cuts, (k1 - k0) / 64);
+          step = ceil_div32(ceil_div32(k1 - k0, q), 64) * 64;
+          k1 = std::min(u.kv_end, k0 + step);
+        }
         // cost: an estimate of the workgroup's time, comparable with the
         // tiled items' (a small-row workgroup streams a key about as fast as
         // a full 128-row tiled one computes it)
