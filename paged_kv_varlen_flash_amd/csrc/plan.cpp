@@ -390,11 +390,11 @@ pa_status plan(const pa_attn_params* p, const int32_t* cu, const int32_t* sk,
           c = ceil_div32(ceil_div32(kv, nsp), 64) * 64;
         }
       }
-      // a split unit's last piece is cut finer (kSmallTailCuts pieces, 2 in
-      // mixed launches), so that the longest-first order ends on short items
-      // and the launch drains faster (D <= 128)
-      const bool graded = force_splits == 0 && kv > chunk && p->head_size <= 128;
-      const int32_t tail_cuts = n_tiled > 0 ? kSmallTailCutsMixed : kSmallTailCuts;
+      // in a mixed launch of the LDS-DMA kernel a split unit's last piece is
+      // cut finer (kSmallTailCutsMixed pieces), so that the longest-first
+      // order ends on short items and the launch drains faster
+      const bool graded = force_splits == 0 && kv > chunk && dma_kernel && n_tiled > 0;
+      const int32_t tail_cuts = kSmallTailCutsMixed;
       int32_t k0 = u.kv_begin;
       int32_t step = std::max(c, 1);
       do {   // (an empty range still gets its item: its rows are written)

@@ -36,14 +36,15 @@ constexpr double kSmallItemsPerCuFp8 = 4.5;
 // 3.5 / 4.5 / 5.5 on the chunked-prefill mix (185.2-186.5 us against
 // 189.1-189.8 us at 3.5; 5.5 within noise of 4.5)
 constexpr double kSmallItemsPerCuDmaMix = 4.5;
-// the last piece of a split small-row unit is cut into this many (at D <=
-// 128): a timestamp probe of the decode batch showed the launch draining
-// over its last third, as equal pieces ended unevenly.  Measured (HIP
-// events, three runs each): chunked-prefill mix 182.6-183.5 us against
-// 185.5-188.5 us with 2 cuts; decode batch 101.3-101.5 us against
-// 101.0-103.6 us with 4 cuts (100.6 against 102.0-102.4 us in another run);
-// at D = 256 (one workgroup per compute unit) finer pieces were slower
-constexpr int32_t kSmallTailCuts = 4;
+// in a mixed launch of the LDS-DMA kernel (bf16 cache, D = 128,
+// power-of-two block size) the last piece of a split small-row unit is cut
+// into this many: a timestamp probe of the decode batch showed a launch
+// draining over its last third, as equal pieces ended unevenly.  Measured
+// (HIP events, three runs each): chunked-prefill mix 182.6-183.5 us against
+// 185.5-188.5 us.  Launches of small items alone keep whole pieces: 4 cuts
+// saved about 1 us of the decode call but doubled its items, and the larger
+// work list and plan made the whole step slower (E4M3 decode step 70 -> 79
+// us); at D = 256 finer pieces were slower
 constexpr int32_t kSmallTailCutsMixed = 2;
 
 static_assert(PA_TILED_ROWS == kTiledWaves * 32, "tiled row block");
