@@ -1204,6 +1204,7 @@ struct TileEntries {
   int e0, e1;
   __device__ int get(int g) const { return g == 0 ? e0 : e1; }
 };
+static_assert(kDmaTileKeys == 32, "TileEntries holds the entries of two 16-key groups");
 
 // Stores one wave's 32 rows of O (lane (n, h) holds, in o[dt][4 ig + e],
 // O^T[d = 32 dt + 8 ig + 4 h + e][row n], already normalised) through an
@@ -1509,7 +1510,7 @@ __device__ __forceinline__ void tiled_dma4_body(const AttnArgs& a, const int32_t
 // tiles.  It measured faster than an 8-wave form with 256-row items sharing
 // each tile, at every length tried (592-1811 and 8192 tokens).
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_tiled_dma4_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 3) void attn_tiled_dma4_kernel(AttnArgs a) {
   constexpr int TILE = kDmaTileKeys * 2 * D;
   __shared__ __attribute__((aligned(1024))) uint8_t lds_a[2 * TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_b[2 * TILE];
@@ -1521,7 +1522,7 @@ __global__ __launch_bounds__(256, 2) void attn_tiled_dma4_kernel(AttnArgs a) {
 // items by the 4-wave LDS-DMA body, three workgroups per compute unit.  The
 // small body's staging area and the K slots share lds_a.
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_mixed_dma_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 3) void attn_mixed_dma_kernel(AttnArgs a) {
   constexpr int TILE = kDmaTileKeys * 2 * D;
   constexpr int LA = small_lds_bytes<D>() > 2 * TILE ? small_lds_bytes<D>() : 2 * TILE;
   __shared__ __attribute__((aligned(1024))) uint8_t lds_a[(LA + 1023) / 1024 * 1024];
